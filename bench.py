@@ -1,0 +1,252 @@
+"""Benchmark of the data-parallel gradient reduce + AdamW step on one MI355X.
+
+One step is the whole path over one batch of synthetic input that is already
+resident in HBM: n*a micro-step accumulations (or none, for incoming
+partials), the replica reduction with fused statistics, the finalisation of
+the per-step scalars and the fused AdamW update of every parameter.
+
+Prints one JSON line: params updated per second (``value``), the achieved HBM
+bandwidth of the whole step under the algorithmic byte model, a roofline entry
+for the dominant kernel (per-launch durations from HIP events recorded on the
+stream the kernels run on) and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+RESIDENT_GRAD_BUDGET = 80e9  # bytes of pre-generated gradients kept in HBM
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gpt2_small",
+                    help="tiny | gpt2_small | zero3_rank_7b | unsharded_7b | tp_column_slice")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 22, help="params in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def bytes_model(w) -> dict:
+    """Algorithmic HBM bytes per parameter of each call kind in one step."""
+    sg = 2.0
+    sp = 2.0
+    per = {}
+    if w.partials:
+        per["reduce"] = w.n * sg + 4.0
+    else:
+        per["accumulate_first"] = w.n * (sg + 4.0)
+        per["accumulate"] = w.n * (w.a - 1) * (sg + 8.0)
+        if w.n > 1:
+            per["reduce"] = 4.0 * w.n + 4.0
+    per["adamw"] = 16.0 + 12.0 + sp
+    return per
+
+
+def launch_bytes(w, kind: str) -> float:
+    """Algorithmic bytes of one launch of `kind` over the whole flat space."""
+    P = float(w.P)
+    if kind == "accumulate_first":
+        return P * (2.0 + 4.0)
+    if kind == "accumulate":
+        return P * (2.0 + 8.0)
+    if kind == "reduce":
+        return P * ((2.0 * w.n if w.partials else 4.0 * w.n) + 4.0)
+    if kind == "adamw":
+        return P * 30.0
+    return 0.0
+
+
+def run_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import synth
+    from gradient_reduce_adam_amd import DP_ROLE_GRAD, dp_plan_bind_flat, driver
+
+    torch.cuda.set_device(0)
+    d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
+                      weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
+                      scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
+                      growth_interval=w.growth_interval, partials=w.partials)
+    st_obj = d.stream
+    stream = st_obj.cuda_stream
+    d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
+
+    # one batch of gradients, resident before the timed region
+    calls = [(r, 1) for r in range(w.n)] if w.partials else [(r, k) for k in range(1, w.a + 1) for r in range(w.n)]
+    per_buf = 2 * w.P
+    nbuf = len(calls) if len(calls) * per_buf <= RESIDENT_GRAD_BUDGET else max(2 if not w.partials else w.n,
+                                                                               int(RESIDENT_GRAD_BUDGET // per_buf))
+    if w.partials:
+        nbuf = max(nbuf, w.n)
+    bufs = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(nbuf)]
+    addr = {}
+    for i, (r, k) in enumerate(calls):
+        b = bufs[i % nbuf]
+        if i < nbuf:
+            synth.grad_device(w.with_(injections=()), 1, r, k, b.data_ptr(), d.scale, stream)
+        addr[(r, k)] = b.data_ptr()
+    torch.cuda.synchronize()
+
+    plan = d.plan
+    events = {}
+
+    def timed(kind, fn, rec):
+        if rec:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st_obj)
+            fn()
+            e1.record(st_obj)
+            events.setdefault(kind, []).append((e0, e1))
+        else:
+            fn()
+
+    def one_step(rec: bool):
+        h = plan.handle
+        if w.partials:
+            for r in range(w.n):
+                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, 1)])
+            timed("reduce", lambda: plan.reduce_replicas("grad", stream=stream), rec)
+        else:
+            for k in range(1, w.a + 1):
+                for r in range(w.n):
+                    dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, k)])
+                    kind = "accumulate_first" if k == 1 else "accumulate"
+                    timed(kind, lambda r=r, k=k: plan.accumulate(r, first=(k == 1),
+                                                                 emit_stats=(w.n == 1 and k == w.a),
+                                                                 stream=stream), rec)
+            if w.n > 1:
+                timed("reduce", lambda: plan.reduce_replicas("acc", stream=stream), rec)
+        timed("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream), rec)
+        timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
+
+    for _ in range(warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    state = d.read_state()
+    per_kind = {}
+    for kind, pairs in events.items():
+        ms = [a.elapsed_time(b) for a, b in pairs]
+        per_kind[kind] = {"launches": len(ms), "avg_ms": sum(ms) / len(ms), "total_ms": sum(ms)}
+    d.close()
+    del bufs
+    torch.cuda.empty_cache()
+    return elapsed, per_kind, state
+
+
+def cpu_baseline(w, sample: int) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload: one
+    full step (all micro-steps, reduction, statistics, update) over `sample`
+    parameters in one tensor, gradients generated beforehand (not timed)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    ws = w.with_(numel=(sample,), injections=(), scaled_tensors=())
+    calls = [(r, 1) for r in range(ws.n)] if ws.partials else [(r, k) for k in range(1, ws.a + 1) for r in range(ws.n)]
+    scale = ws.init_scale if ws.scaler != "none" else 1.0
+    pre = {rk: synth.grad_host(ws, 1, rk[0], rk[1], 0, sample, scale, threads=threads) for rk in calls}
+    master = synth.master_host(ws, 0, sample, threads=threads)
+
+    def grad_fn(step, r, k, lo, hi, sc):
+        return pre[(r, k)][lo:hi]
+
+    t0 = time.perf_counter()
+    oracle.run(ws, 1, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step of {ws.name} (n={ws.n}, a={ws.a}) over {sample} params in one tensor, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    from synth import workloads
+
+    w = workloads.by_name(args.workload)
+    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup)
+    ms_per_step = elapsed * 1e3 / args.steps
+    per_param = bytes_model(w)
+    step_bytes = sum(per_param.values()) * w.P
+    hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the call kind that moves the most algorithmic bytes per step
+    dom = max(per_param, key=lambda k: per_param[k])
+    dom_bytes = launch_bytes(w, dom)
+    dom_ms = per_kind[dom]["avg_ms"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        ent = t.get(w.name, {}).get(dom)
+        if ent and ent.get("kernel_source_sha") == kernel_source_hash():
+            traffic = ent["bytes_per_launch"]
+
+    line = {
+        "metric": "params updated/sec and achieved HBM GB/s (% of peak) per full DP step",
+        "value": w.P * args.steps / elapsed,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "params": w.P, "tensors": w.T, "n_replicas": w.n, "micro_steps": w.a,
+                   "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "state": "fp32 master/m/v",
+                   "update_arithmetic": "f64", "clip": w.max_norm, "loss_scale": w.scaler,
+                   "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)"},
+        "hbm_gbps": hbm_gbps,
+        "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
+        "bytes_per_param_step": sum(per_param.values()),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "bytes_per_launch": dom_bytes,
+                     "avg_launch_ms": dom_ms},
+        "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
+        "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

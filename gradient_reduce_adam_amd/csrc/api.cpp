@@ -1,0 +1,509 @@
+// C ABI of the data-parallel gradient reduce + AdamW step: plans, chunk
+// tables, bindings, argument checks and the ordering rules between calls.
+// The kernels live in kernels.hip; this file only validates and launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dp_internal.h"
+#include "dpstep.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dp_status fail(dp_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+dp_status hip_fail(hipError_t e, const char* what) {
+    return fail(DP_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+constexpr int kNumRoles = 7;
+
+struct Binding {
+    void* flat = nullptr;
+    std::vector<void*> tensors;
+    void** dev_table = nullptr;
+    bool bound = false;
+
+    dpk::RoleRef ref() const { return dpk::RoleRef{flat, dev_table}; }
+};
+
+struct DeviceTable {
+    int64_t begin = 0, end = 0, count = 0;
+    dp_chunk* dev = nullptr;
+};
+
+size_t esize(dp_dtype d) { return d == DP_F32 ? 4 : 2; }
+
+}  // namespace
+
+struct dp_plan {
+    std::vector<int64_t> numel, prefix;
+    int64_t P = 0;
+    int32_t T = 0, n = 1, chunk = DP_DEFAULT_CHUNK;
+    dp_dtype gdt = DP_BF16, pdt = DP_BF16;
+
+    Binding roles[kNumRoles][DP_MAX_REPLICAS];
+
+    // device resources (allocated by dp_state_init / prepare / bind_tensors)
+    int device = -1;
+    dpk::DevState* state = nullptr;
+    dpk::StatsBuf stats{nullptr, nullptr};
+    DeviceTable full;
+    std::vector<DeviceTable> ranges;
+
+    // ordering state
+    bool state_ready = false;
+    dp_state_cfg cfg{};
+    std::vector<int32_t> micro;   // micro-steps accumulated per replica since the last reduction
+    bool partials_valid = false;  // chunk statistics of the current g_bar exist
+    bool stats_current = false;   // dp_grad_stats ran on the current g_bar
+};
+
+namespace {
+
+// Chunk table of [begin, end): every tensor piece inside the range, split at
+// multiples of chunk_elems counted from the tensor's start (so a chunk keeps
+// the tensor's alignment), in flat order.
+void build_chunks(const dp_plan* p, int64_t begin, int64_t end, std::vector<dp_chunk>* out) {
+    out->clear();
+    if (begin >= end) return;
+    int32_t t = static_cast<int32_t>(std::upper_bound(p->prefix.begin(), p->prefix.end(), begin) - p->prefix.begin()) - 1;
+    for (; t < p->T && p->prefix[t] < end; ++t) {
+        const int64_t t0 = p->prefix[t], t1 = p->prefix[t + 1];
+        const int64_t lo = std::max(begin, t0), hi = std::min(end, t1);
+        if (lo >= hi) continue;
+        int64_t off = lo - t0;
+        while (off < hi - t0) {
+            const int64_t next = (off / p->chunk + 1) * p->chunk;
+            const int64_t stop = std::min(next, hi - t0);
+            out->push_back(dp_chunk{t0 + off, off, t, static_cast<int32_t>(stop - off)});
+            off = stop;
+        }
+    }
+}
+
+dp_status ensure_device(dp_plan* p) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (p->device >= 0 && p->device != dev)
+        return fail(DP_ERR_STATE, "plan was set up on device %d, current device is %d", p->device, dev);
+    p->device = dev;
+    return DP_OK;
+}
+
+dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out) {
+    std::vector<dp_chunk> host;
+    build_chunks(p, begin, end, &host);
+    out->begin = begin;
+    out->end = end;
+    out->count = static_cast<int64_t>(host.size());
+    out->dev = nullptr;
+    if (host.empty()) return DP_OK;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&out->dev), host.size() * sizeof(dp_chunk));
+    if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of a %zu-entry chunk table: %s", host.size(), hipGetErrorString(e));
+    e = hipMemcpy(out->dev, host.data(), host.size() * sizeof(dp_chunk), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(out->dev);
+        out->dev = nullptr;
+        return hip_fail(e, "hipMemcpy of a chunk table");
+    }
+    return DP_OK;
+}
+
+dp_status ensure_full(dp_plan* p) {
+    if (p->full.dev || p->P == 0 || p->full.count > 0) return DP_OK;
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
+    return upload_table(p, 0, p->P, &p->full);
+}
+
+dp_status range_table(dp_plan* p, int64_t begin, int64_t end, const DeviceTable** out) {
+    if (begin == 0 && end == p->P) {
+        dp_status s = ensure_full(p);
+        *out = &p->full;
+        return s;
+    }
+    for (const DeviceTable& t : p->ranges)
+        if (t.begin == begin && t.end == end) {
+            *out = &t;
+            return DP_OK;
+        }
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
+    DeviceTable t;
+    s = upload_table(p, begin, end, &t);
+    if (s != DP_OK) return s;
+    p->ranges.push_back(t);
+    *out = &p->ranges.back();
+    return DP_OK;
+}
+
+bool role_ok(dp_role r) { return r >= DP_ROLE_PARAM && r <= DP_ROLE_GBAR; }
+bool per_replica(dp_role r) { return r == DP_ROLE_GRAD || r == DP_ROLE_ACC; }
+
+const Binding* gbar_binding(const dp_plan* p) {
+    const Binding* b = &p->roles[DP_ROLE_GBAR][0];
+    if (!b->bound && p->n == 1) b = &p->roles[DP_ROLE_ACC][0];
+    return b;
+}
+
+dp_status need(const Binding* b, const char* what) {
+    if (!b->bound) return fail(DP_ERR_UNBOUND, "role %s is not bound", what);
+    return DP_OK;
+}
+
+dp_status check_launch(hipError_t e, const char* what) { return e == hipSuccess ? DP_OK : hip_fail(e, what); }
+
+}  // namespace
+
+extern "C" {
+
+int dp_abi_version(void) { return DP_ABI_VERSION; }
+
+const char* dp_status_string(dp_status s) {
+    switch (s) {
+        case DP_OK: return "ok";
+        case DP_ERR_INVALID_ARG: return "invalid argument";
+        case DP_ERR_BAD_LAYOUT: return "bad layout";
+        case DP_ERR_UNBOUND: return "role not bound";
+        case DP_ERR_RANGE: return "range out of bounds";
+        case DP_ERR_STATE: return "call out of order";
+        case DP_ERR_OOM: return "out of memory";
+        case DP_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* dp_last_error(void) { return g_last_error.c_str(); }
+
+dp_status dp_plan_create(const dp_layout* L, dp_plan** out) {
+    if (!L || !out) return fail(DP_ERR_INVALID_ARG, "dp_plan_create: null argument");
+    *out = nullptr;
+    if (L->num_tensors < 0) return fail(DP_ERR_BAD_LAYOUT, "num_tensors %d < 0", L->num_tensors);
+    if (L->num_tensors > 0 && !L->numel) return fail(DP_ERR_BAD_LAYOUT, "numel is null");
+    if (L->n_replicas < 1 || L->n_replicas > DP_MAX_REPLICAS)
+        return fail(DP_ERR_BAD_LAYOUT, "n_replicas %d outside [1, %d]", L->n_replicas, DP_MAX_REPLICAS);
+    if (L->grad_dtype != DP_F16 && L->grad_dtype != DP_BF16)
+        return fail(DP_ERR_BAD_LAYOUT, "grad_dtype must be DP_F16 or DP_BF16");
+    if (L->param_dtype != DP_F16 && L->param_dtype != DP_BF16)
+        return fail(DP_ERR_BAD_LAYOUT, "param_dtype must be DP_F16 or DP_BF16");
+    int32_t chunk = L->chunk_elems == 0 ? DP_DEFAULT_CHUNK : L->chunk_elems;
+    if (chunk < 256 || chunk > (1 << 26) || chunk % 256 != 0)
+        return fail(DP_ERR_BAD_LAYOUT, "chunk_elems %d must be a multiple of 256 in [256, 2^26]", L->chunk_elems);
+    dp_plan* p = new (std::nothrow) dp_plan();
+    if (!p) return fail(DP_ERR_OOM, "dp_plan_create: host allocation failed");
+    p->T = L->num_tensors;
+    p->n = L->n_replicas;
+    p->gdt = L->grad_dtype;
+    p->pdt = L->param_dtype;
+    p->chunk = chunk;
+    p->numel.assign(L->numel, L->numel + L->num_tensors);
+    p->prefix.assign(static_cast<size_t>(p->T) + 1, 0);
+    for (int32_t i = 0; i < p->T; ++i) {
+        if (p->numel[i] < 0) {
+            delete p;
+            return fail(DP_ERR_BAD_LAYOUT, "numel[%d] = %lld < 0", i, static_cast<long long>(L->numel[i]));
+        }
+        if (p->prefix[i] > INT64_MAX / 2 - p->numel[i]) {
+            delete p;
+            return fail(DP_ERR_BAD_LAYOUT, "total parameter count overflows");
+        }
+        p->prefix[i + 1] = p->prefix[i] + p->numel[i];
+    }
+    p->P = p->prefix[p->T];
+    p->micro.assign(p->n, 0);
+    *out = p;
+    return DP_OK;
+}
+
+dp_status dp_plan_destroy(dp_plan* p) {
+    if (!p) return DP_OK;
+    if (p->device >= 0) {
+        (void)hipDeviceSynchronize();
+        for (auto& row : p->roles)
+            for (auto& b : row)
+                if (b.dev_table) (void)hipFree(b.dev_table);
+        if (p->full.dev) (void)hipFree(p->full.dev);
+        for (auto& t : p->ranges)
+            if (t.dev) (void)hipFree(t.dev);
+        if (p->state) (void)hipFree(p->state);
+        if (p->stats.sumsq) (void)hipFree(p->stats.sumsq);
+        if (p->stats.bad) (void)hipFree(p->stats.bad);
+    }
+    delete p;
+    return DP_OK;
+}
+
+dp_status dp_plan_info_get(const dp_plan* p, dp_plan_info* out) {
+    if (!p || !out) return fail(DP_ERR_INVALID_ARG, "dp_plan_info_get: null argument");
+    std::vector<dp_chunk> tmp;
+    build_chunks(p, 0, p->P, &tmp);
+    const double P = static_cast<double>(p->P);
+    const double sg = static_cast<double>(esize(p->gdt)), sp = static_cast<double>(esize(p->pdt));
+    out->params = p->P;
+    out->num_chunks = static_cast<int64_t>(tmp.size());
+    out->num_tensors = p->T;
+    out->n_replicas = p->n;
+    out->chunk_elems = p->chunk;
+    out->reserved = 0;
+    out->state_bytes = 16.0 * P;
+    out->bytes_accumulate_first = P * (sg + 4.0);
+    out->bytes_accumulate = P * (sg + 8.0);
+    out->bytes_reduce_acc = P * (4.0 * p->n + 4.0);
+    out->bytes_reduce_partials = P * (sg * p->n + 4.0);
+    out->bytes_stats_scan = P * 4.0;
+    out->bytes_adam = P * (16.0 + 12.0 + sp);
+    return DP_OK;
+}
+
+dp_status dp_plan_chunks(const dp_plan* p, int64_t begin, int64_t end, int64_t first, int64_t cap, dp_chunk* out,
+                         int64_t* count) {
+    if (!p || !count || (cap > 0 && !out) || first < 0 || cap < 0)
+        return fail(DP_ERR_INVALID_ARG, "dp_plan_chunks: bad argument");
+    if (begin < 0 || end > p->P || begin > end)
+        return fail(DP_ERR_RANGE, "range [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
+                    static_cast<long long>(end), static_cast<long long>(p->P));
+    std::vector<dp_chunk> tmp;
+    build_chunks(p, begin, end, &tmp);
+    *count = static_cast<int64_t>(tmp.size());
+    for (int64_t i = 0; i < cap && first + i < *count; ++i) out[i] = tmp[static_cast<size_t>(first + i)];
+    return DP_OK;
+}
+
+static dp_status bind_check(dp_plan* p, dp_role role, int32_t replica) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "bind: null plan");
+    if (!role_ok(role)) return fail(DP_ERR_INVALID_ARG, "bind: unknown role %d", static_cast<int>(role));
+    const int32_t lim = per_replica(role) ? p->n : 1;
+    if (replica < 0 || replica >= lim)
+        return fail(DP_ERR_INVALID_ARG, "bind: replica %d outside [0, %d) for role %d", replica, lim, static_cast<int>(role));
+    return DP_OK;
+}
+
+dp_status dp_plan_bind_flat(dp_plan* p, dp_role role, int32_t replica, void* base) {
+    dp_status s = bind_check(p, role, replica);
+    if (s != DP_OK) return s;
+    if (!base && p->P > 0) return fail(DP_ERR_INVALID_ARG, "bind_flat: null base");
+    Binding& b = p->roles[role][replica];
+    b.flat = base;
+    b.tensors.clear();
+    if (b.dev_table) {
+        (void)hipFree(b.dev_table);
+        b.dev_table = nullptr;
+    }
+    b.bound = true;
+    return DP_OK;
+}
+
+dp_status dp_plan_bind_tensors(dp_plan* p, dp_role role, int32_t replica, void* const* ptrs) {
+    dp_status s = bind_check(p, role, replica);
+    if (s != DP_OK) return s;
+    if (p->T > 0 && !ptrs) return fail(DP_ERR_INVALID_ARG, "bind_tensors: null pointer array");
+    for (int32_t i = 0; i < p->T; ++i)
+        if (!ptrs[i] && p->numel[i] > 0) return fail(DP_ERR_INVALID_ARG, "bind_tensors: tensor %d has a null pointer", i);
+    s = ensure_device(p);
+    if (s != DP_OK) return s;
+    Binding& b = p->roles[role][replica];
+    if (!b.dev_table && p->T > 0) {
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&b.dev_table), sizeof(void*) * p->T);
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of a pointer table: %s", hipGetErrorString(e));
+    }
+    b.tensors.assign(ptrs, ptrs + p->T);
+    if (p->T > 0) {
+        hipError_t e = hipMemcpy(b.dev_table, b.tensors.data(), sizeof(void*) * p->T, hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy of a pointer table");
+    }
+    b.flat = nullptr;
+    b.bound = true;
+    return DP_OK;
+}
+
+dp_status dp_plan_prepare_range(dp_plan* p, int64_t begin, int64_t end) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "prepare_range: null plan");
+    if (begin < 0 || end > p->P || begin > end)
+        return fail(DP_ERR_RANGE, "range [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
+                    static_cast<long long>(end), static_cast<long long>(p->P));
+    const DeviceTable* t = nullptr;
+    return range_table(p, begin, end, &t);
+}
+
+dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream) {
+    if (!p || !cfg) return fail(DP_ERR_INVALID_ARG, "dp_state_init: null argument");
+    if (cfg->scaler_mode < DP_SCALER_NONE || cfg->scaler_mode > DP_SCALER_DYNAMIC)
+        return fail(DP_ERR_INVALID_ARG, "unknown scaler_mode %d", cfg->scaler_mode);
+    if (!(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0 && cfg->beta2 >= 0.0 && cfg->beta2 < 1.0))
+        return fail(DP_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+    if (cfg->scaler_mode != DP_SCALER_NONE && !(cfg->init_scale > 0.0))
+        return fail(DP_ERR_INVALID_ARG, "init_scale must be > 0");
+    if (cfg->scaler_mode == DP_SCALER_DYNAMIC &&
+        (!(cfg->backoff > 0.0 && cfg->backoff < 1.0) || !(cfg->growth >= 1.0) || cfg->growth_interval <= 0))
+        return fail(DP_ERR_INVALID_ARG, "dynamic scaler needs backoff in (0,1), growth >= 1, growth_interval > 0");
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
+    s = ensure_full(p);
+    if (s != DP_OK) return s;
+    if (!p->state) {
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->state), sizeof(dpk::DevState));
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of the state block: %s", hipGetErrorString(e));
+        const size_t np = static_cast<size_t>(std::max<int64_t>(p->full.count, 1));
+        e = hipMalloc(reinterpret_cast<void**>(&p->stats.sumsq), np * sizeof(double));
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
+        e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
+    }
+    const double scale = cfg->scaler_mode == DP_SCALER_NONE ? 1.0 : cfg->init_scale;
+    s = check_launch(dpk::launch_state_init(p->state, scale, stream), "state init launch");
+    if (s != DP_OK) return s;
+    p->cfg = *cfg;
+    p->state_ready = true;
+    std::fill(p->micro.begin(), p->micro.end(), 0);
+    p->partials_valid = false;
+    p->stats_current = false;
+    return DP_OK;
+}
+
+dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit_stats, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate: null plan");
+    if (replica < 0 || replica >= p->n) return fail(DP_ERR_INVALID_ARG, "replica %d outside [0, %d)", replica, p->n);
+    if (emit_stats && p->n != 1)
+        return fail(DP_ERR_INVALID_ARG, "emit_stats needs n_replicas == 1 (g_bar is then the accumulator)");
+    const Binding& g = p->roles[DP_ROLE_GRAD][replica];
+    const Binding& a = p->roles[DP_ROLE_ACC][replica];
+    dp_status s = need(&g, "GRAD");
+    if (s == DP_OK) s = need(&a, "ACC");
+    if (s != DP_OK) return s;
+    if (emit_stats) {
+        const Binding* gb = gbar_binding(p);
+        if (gb->flat != a.flat || gb->dev_table != a.dev_table)
+            return fail(DP_ERR_STATE, "emit_stats needs GBAR to be ACC[0] (leave GBAR unbound)");
+        if (!p->state_ready) return fail(DP_ERR_STATE, "emit_stats before dp_state_init");
+    }
+    if (!first && p->micro[replica] == 0)
+        return fail(DP_ERR_STATE, "replica %d: first == 0 without a first micro-step since the last reduction", replica);
+    s = ensure_full(p);
+    if (s != DP_OK) return s;
+    if (p->full.count > 0) {
+        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, p->full.dev, p->full.count,
+                                                g.ref(), a.ref(), p->stats, stream),
+                         "accumulate launch");
+        if (s != DP_OK) return s;
+    }
+    p->micro[replica] = first ? 1 : p->micro[replica] + 1;
+    p->stats_current = false;
+    p->partials_valid = emit_stats != 0;
+    return DP_OK;
+}
+
+dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_replicas: null plan");
+    if (src != DP_ROLE_ACC && src != DP_ROLE_GRAD)
+        return fail(DP_ERR_INVALID_ARG, "src must be DP_ROLE_ACC or DP_ROLE_GRAD");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_replicas before dp_state_init");
+    dpk::Srcs srcs{};
+    for (int32_t r = 0; r < p->n; ++r) {
+        const Binding& b = p->roles[src][r];
+        if (!b.bound) return fail(DP_ERR_UNBOUND, "role %s of replica %d is not bound", src == DP_ROLE_ACC ? "ACC" : "GRAD", r);
+        srcs.r[r] = b.ref();
+    }
+    if (src == DP_ROLE_ACC) {
+        for (int32_t r = 0; r < p->n; ++r)
+            if (p->micro[r] != p->micro[0] || p->micro[r] == 0)
+                return fail(DP_ERR_STATE, "replicas accumulated different numbers of micro-steps (replica %d: %d, replica 0: %d)",
+                            r, p->micro[r], p->micro[0]);
+    }
+    const Binding* gb = gbar_binding(p);
+    if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
+    dp_status s = ensure_full(p);
+    if (s != DP_OK) return s;
+    if (p->full.count > 0) {
+        s = check_launch(dpk::launch_reduce(src == DP_ROLE_ACC ? DP_F32 : p->gdt, p->n, p->full.dev, p->full.count, srcs,
+                                            gb->ref(), p->stats, stream),
+                         "reduce launch");
+        if (s != DP_OK) return s;
+    }
+    std::fill(p->micro.begin(), p->micro.end(), 0);
+    p->partials_valid = true;
+    p->stats_current = false;
+    return DP_OK;
+}
+
+dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_grad_stats: null plan");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_grad_stats before dp_state_init");
+    if (!(max_norm >= 0.0)) return fail(DP_ERR_INVALID_ARG, "max_norm must be >= 0 (0 disables clipping)");
+    dp_status s = ensure_full(p);
+    if (s != DP_OK) return s;
+    if (scan) {
+        const Binding* gb = gbar_binding(p);
+        s = need(gb, "GBAR");
+        if (s != DP_OK) return s;
+        if (p->full.count > 0) {
+            s = check_launch(dpk::launch_stats(p->full.dev, p->full.count, gb->ref(), p->stats, stream), "stats launch");
+            if (s != DP_OK) return s;
+        }
+    } else if (!p->partials_valid && p->full.count > 0) {
+        return fail(DP_ERR_STATE, "no fused statistics for the current g_bar: reduce first, or pass scan = 1");
+    }
+    dpk::ScalerArgs a{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, max_norm,
+                      p->cfg.scaler_mode, p->cfg.growth_interval};
+    s = check_launch(dpk::launch_finalize(p->stats, p->full.count, p->state, a, stream), "finalize launch");
+    if (s != DP_OK) return s;
+    p->partials_valid = false;
+    p->stats_current = true;
+    std::fill(p->micro.begin(), p->micro.end(), 0);
+    return DP_OK;
+}
+
+dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int64_t end, hipStream_t stream) {
+    if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_adam_step: null argument");
+    if (begin < 0 || end > p->P || begin > end)
+        return fail(DP_ERR_RANGE, "shard [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
+                    static_cast<long long>(end), static_cast<long long>(p->P));
+    if (!(hp->lr >= 0.0) || !(hp->eps > 0.0) || !(hp->weight_decay >= 0.0))
+        return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
+    if (!p->stats_current) return fail(DP_ERR_STATE, "dp_adam_step before dp_grad_stats on the current g_bar");
+    const Binding* gb = gbar_binding(p);
+    dp_status s = need(gb, "GBAR");
+    if (s == DP_OK) s = need(&p->roles[DP_ROLE_MASTER][0], "MASTER");
+    if (s == DP_OK) s = need(&p->roles[DP_ROLE_EXP_AVG][0], "EXP_AVG");
+    if (s == DP_OK) s = need(&p->roles[DP_ROLE_EXP_AVG_SQ][0], "EXP_AVG_SQ");
+    if (s == DP_OK) s = need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
+    if (s != DP_OK) return s;
+    if (begin == end) return DP_OK;
+    const DeviceTable* t = nullptr;
+    s = range_table(p, begin, end, &t);
+    if (s != DP_OK) return s;
+    dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
+    return check_launch(dpk::launch_adamw(p->pdt, t->dev, t->count, gb->ref(), p->roles[DP_ROLE_MASTER][0].ref(),
+                                          p->roles[DP_ROLE_EXP_AVG][0].ref(), p->roles[DP_ROLE_EXP_AVG_SQ][0].ref(),
+                                          p->roles[DP_ROLE_PARAM][0].ref(), p->state, a, stream),
+                        "adamw launch");
+}
+
+dp_status dp_read_state(dp_plan* p, dp_step_state* out, hipStream_t stream) {
+    if (!p || !out) return fail(DP_ERR_INVALID_ARG, "dp_read_state: null argument");
+    if (!p->state) return fail(DP_ERR_STATE, "dp_read_state before dp_state_init");
+    hipError_t e = hipMemcpyAsync(out, p->state, sizeof(dp_step_state), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the state block");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return DP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+"""A whole data-parallel step on one GPU through the C ABI.
+
+``DPStep`` allocates the state in HBM with torch (memory only), binds it to a
+plan and issues, per step: n*a ``dp_accumulate`` calls (or, for incoming
+low-precision partials, none), one ``dp_reduce_replicas``, one
+``dp_grad_stats`` and one ``dp_adam_step`` per shard range.  Gradients come
+from a caller-supplied producer, standing in for the backward pass.
+
+HBM layout (flat parameter space of P elements, tensors in list order):
+master, exp_avg, exp_avg_sq: binary32 [P]; param: bf16/fp16 [P];
+acc[r]: binary32 [P] per replica (absent for partials; with n = 1, acc[0] is
+also g_bar); gbar: binary32 [P] when n > 1 or with partials; gradients: the
+producer's buffers, bound per call.
+"""
+from __future__ import annotations
+
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import DP_ROLE_GRAD, Plan, dp_plan_bind_flat
+
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+# producer(step, replica, micro, loss_scale) -> device address of that gradient
+GradProducer = Callable[[int, int, int, float], int]
+
+
+def even_shards(P: int, shards: int) -> List[Tuple[int, int]]:
+    cuts = [P * i // shards for i in range(shards + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(shards)]
+
+
+class DPStep:
+    def __init__(self, numel: Sequence[int], n: int, a: int, grad_dtype: str, param_dtype: str, *,
+                 lr: float = 1e-3, eps: float = 1e-8, weight_decay: float = 0.01, beta1: float = 0.9,
+                 beta2: float = 0.999, max_norm: float = 0.0, scaler: str = "none", init_scale: float = 1.0,
+                 backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, partials: bool = False,
+                 shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
+                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None):
+        if partials and a != 1:
+            raise ValueError("incoming partials are reduced directly: a must be 1")
+        self.n, self.a, self.partials = n, a, partials
+        self.lr, self.eps, self.weight_decay, self.max_norm = lr, eps, weight_decay, max_norm
+        self.scaler = scaler
+        self.plan = Plan(numel, n, grad_dtype, param_dtype, chunk_elems)
+        P = self.P = self.plan.P
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.master = torch.zeros(P, **f32)
+        self.exp_avg = torch.zeros(P, **f32)
+        self.exp_avg_sq = torch.zeros(P, **f32)
+        self.param = torch.zeros(P, dtype=TORCH_DTYPES[param_dtype], device=self.device)
+        self.acc: List[torch.Tensor] = [] if partials else [torch.zeros(P, **f32) for _ in range(n)]
+        self.gbar = self.acc[0] if (n == 1 and not partials) else torch.zeros(P, **f32)
+        pl = self.plan
+        pl.bind("master", self.master)
+        pl.bind("exp_avg", self.exp_avg)
+        pl.bind("exp_avg_sq", self.exp_avg_sq)
+        pl.bind("param", self.param)
+        for r, t in enumerate(self.acc):
+            pl.bind("acc", t, r)
+        if self.gbar is not (self.acc[0] if self.acc else None):
+            pl.bind("gbar", self.gbar)
+        self.shards = list(shards) if shards is not None else [(0, P)]
+        for b, e in self.shards:
+            pl.prepare_range(b, e)
+        pl.state_init(beta1, beta2, scaler, init_scale, backoff, growth, growth_interval, stream=self.stream)
+        self.scale = 1.0 if scaler == "none" else float(init_scale)
+        self.steps_done = 0
+
+    # -- setup ------------------------------------------------------------
+    def set_master(self, fill: Callable[[int], None]) -> None:
+        """fill(address) writes the initial binary32 master weights; the
+        low-precision copy starts as their round-to-nearest-even image."""
+        fill(self.master.data_ptr())
+        torch.cuda.current_stream(self.device).wait_stream(self.stream)
+        self.param.copy_(self.master.to(self.param.dtype))
+
+    # -- one step ---------------------------------------------------------
+    def issue_gradients(self, produce: GradProducer, step: int) -> None:
+        """The accumulation (or partial) part of a step, up to g_bar."""
+        pl, st = self.plan, self.stream.cuda_stream
+        if self.partials:
+            for r in range(self.n):
+                dp_plan_bind_flat(pl.handle, DP_ROLE_GRAD, r, produce(step, r, 1, self.scale))
+            pl.reduce_replicas("grad", stream=st)
+            return
+        for k in range(1, self.a + 1):
+            for r in range(self.n):
+                dp_plan_bind_flat(pl.handle, DP_ROLE_GRAD, r, produce(step, r, k, self.scale))
+                pl.accumulate(r, first=(k == 1), emit_stats=(self.n == 1 and k == self.a), stream=st)
+        if self.n > 1:
+            pl.reduce_replicas("acc", stream=st)
+
+    def finish(self) -> None:
+        """Statistics, scalars and the update on every shard range."""
+        pl, st = self.plan, self.stream.cuda_stream
+        pl.grad_stats(scan=False, max_norm=self.max_norm, stream=st)
+        for b, e in self.shards:
+            pl.adam_step(self.lr, self.eps, self.weight_decay, b, e, stream=st)
+
+    def step(self, produce: GradProducer, sync_scale: bool = True) -> Optional[dict]:
+        self.steps_done += 1
+        self.issue_gradients(produce, self.steps_done)
+        self.finish()
+        if sync_scale:
+            s = self.read_state()
+            self.scale = s["scale"]
+            return s
+        return None
+
+    def read_state(self) -> dict:
+        return self.plan.read_state(stream=self.stream.cuda_stream)
+
+    def close(self) -> None:
+        self.plan.close()

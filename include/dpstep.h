@@ -1,0 +1,246 @@
+/*
+ * dpstep.h -- C ABI of the data-parallel gradient reduce + AdamW step for
+ * MI355X (gfx950).
+ *
+ * The step, as the pages define it:
+ *  - every replica r holds the full model and accumulates the gradients of
+ *    its a micro-steps into g_r, with no communication in between
+ *    ("Distributed Training: Split along the Four Axes of Data, Tensor,
+ *    Pipeline, and State", ai-knowledge-map.com: averaging-formula paragraph
+ *    and the b=4, a=8, n=8 worked example);
+ *  - the replicas are averaged, g_bar = (sum_r g_r) / n, and every replica
+ *    applies the same update with it (same page: data-parallel all-reduce and
+ *    averaging-formula paragraphs);
+ *  - the update keeps a higher-precision master copy and Adam's two moments
+ *    beside the low-precision weights, 16 bytes per parameter in all (same
+ *    page, mixed-precision paragraph; "Data vs Tensor vs Pipeline
+ *    Parallelism: When to Use Each", abhik.ai, section "What each one splits
+ *    / Data parallelism");
+ *  - under ZeRO a rank updates only its shard of the state, with the same
+ *    result as the unsharded update (first page, ZeRO paragraph; second page,
+ *    same section: 16*Psi/N bytes per GPU).
+ *
+ * Here the n replicas are n buffers in one GPU's memory and a shard is a
+ * range [shard_begin, shard_end) of the flat parameter space: the
+ * concatenation of the plan's tensors in list order.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named device point to GPU memory the caller owns (allocated by
+ *    any means, for example by torch); the library never frees them.  Pointers
+ *    named host point to host memory, read during the call only.
+ *  - Compute calls are asynchronous on the caller's stream, never synchronise
+ *    and never allocate, except where a comment says otherwise.
+ *  - Every call returns a dp_status.  On failure nothing was launched and
+ *    dp_last_error() returns a message for the calling thread.  Faults inside
+ *    kernels surface at the next synchronising call (dp_read_state).
+ *  - One plan is used from one stream at a time; distinct plans are
+ *    independent.
+ */
+#ifndef DPSTEP_H
+#define DPSTEP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DP_ABI_VERSION 1
+#define DP_MAX_REPLICAS 16
+#define DP_DEFAULT_CHUNK 65536
+
+typedef enum dp_status {
+    DP_OK = 0,
+    DP_ERR_INVALID_ARG = 1, /* null pointer, unknown enum value, bad size */
+    DP_ERR_BAD_LAYOUT = 2,  /* layout rejected by dp_plan_create */
+    DP_ERR_UNBOUND = 3,     /* a role the call reads or writes has no memory bound */
+    DP_ERR_RANGE = 4,       /* range not inside [0, P) or begin > end */
+    DP_ERR_STATE = 5,       /* call out of order (see each call) */
+    DP_ERR_OOM = 6,         /* a library allocation failed */
+    DP_ERR_HIP = 7          /* a HIP call failed; dp_last_error() has its text */
+} dp_status;
+
+typedef enum dp_dtype { DP_F32 = 0, DP_F16 = 1, DP_BF16 = 2 } dp_dtype;
+
+/* Memory roles.  All roles are laid out like the flat parameter space. */
+typedef enum dp_role {
+    DP_ROLE_PARAM = 0,      /* low-precision parameters (param dtype); written by dp_adam_step */
+    DP_ROLE_MASTER = 1,     /* binary32 master weights */
+    DP_ROLE_EXP_AVG = 2,    /* binary32 first moment m */
+    DP_ROLE_EXP_AVG_SQ = 3, /* binary32 second moment v */
+    DP_ROLE_GRAD = 4,       /* per replica: the micro-step gradient, or the incoming partial (grad dtype) */
+    DP_ROLE_ACC = 5,        /* per replica: binary32 accumulator g_r */
+    DP_ROLE_GBAR = 6        /* binary32 averaged gradient g_bar; with n = 1 it defaults to ACC[0] */
+} dp_role;
+
+typedef enum dp_scaler_mode {
+    DP_SCALER_NONE = 0,    /* scale 1; a non-finite gradient still skips the step */
+    DP_SCALER_STATIC = 1,  /* fixed scale; a non-finite gradient skips the step */
+    DP_SCALER_DYNAMIC = 2  /* skip and back off on a non-finite gradient, grow after growth_interval clean steps */
+} dp_scaler_mode;
+
+/* Ragged tensor list.  numel is host memory, copied by dp_plan_create. */
+typedef struct dp_layout {
+    int32_t num_tensors;   /* >= 0 */
+    int32_t n_replicas;    /* 1 .. DP_MAX_REPLICAS */
+    const int64_t* numel;  /* host: [num_tensors], each >= 0 */
+    dp_dtype grad_dtype;   /* DP_F16 or DP_BF16 */
+    dp_dtype param_dtype;  /* DP_F16 or DP_BF16 */
+    int32_t chunk_elems;   /* 0 = DP_DEFAULT_CHUNK; else a multiple of 256 in [256, 2^26] */
+    int32_t reserved;
+} dp_layout;
+
+typedef struct dp_state_cfg {
+    double beta1, beta2;       /* Adam's moment decay rates */
+    int32_t scaler_mode;       /* dp_scaler_mode */
+    int32_t growth_interval;   /* dynamic: clean steps before the scale grows (> 0) */
+    double init_scale;         /* static / dynamic: initial loss scale (> 0) */
+    double backoff;            /* dynamic: factor on a skipped step, in (0, 1) */
+    double growth;             /* dynamic: growth factor, >= 1 */
+} dp_state_cfg;
+
+typedef struct dp_adam_hparams {
+    double lr;            /* learning rate */
+    double eps;           /* added to sqrt of the bias-corrected second moment */
+    double weight_decay;  /* decoupled: w <- w * (1 - lr * weight_decay) */
+} dp_adam_hparams;
+
+/* The per-run scalar state, as held on the device. */
+typedef struct dp_step_state {
+    int64_t t;               /* applied updates */
+    int64_t iter;            /* steps taken, applied or skipped */
+    int64_t growth_tracker;  /* consecutive applied steps since the last scale change */
+    double beta1_pow;        /* beta1^t */
+    double beta2_pow;        /* beta2^t */
+    double scale;            /* loss scale the next step's gradients must carry */
+    int32_t found_inf;       /* the last finalised g_bar held an inf or NaN: the step was skipped */
+    int32_t reserved;
+    double sumsq;            /* sum of squares of the last (scaled) g_bar */
+    double norm;             /* L2 norm of the last unscaled g_bar */
+    double clip;             /* global-norm clip factor applied (1 when off or not needed) */
+    double gscale;           /* clip / scale: multiplies the stored g_bar in the update */
+} dp_step_state;
+
+typedef struct dp_plan_info {
+    int64_t params;          /* P */
+    int64_t num_chunks;      /* chunks covering [0, P) */
+    int32_t num_tensors;
+    int32_t n_replicas;
+    int32_t chunk_elems;
+    int32_t reserved;
+    double state_bytes;      /* 16 * P: param + grad (2 + 2) + master, m, v (4 + 4 + 4) */
+    /* algorithmic HBM bytes of one call over the full range */
+    double bytes_accumulate_first;  /* read g, write g_r */
+    double bytes_accumulate;        /* read g and g_r, write g_r */
+    double bytes_reduce_acc;        /* read n accumulators, write g_bar */
+    double bytes_reduce_partials;   /* read n low-precision partials, write g_bar */
+    double bytes_stats_scan;        /* read g_bar */
+    double bytes_adam;              /* read g_bar, w, m, v; write w, m, v, p */
+} dp_plan_info;
+
+/* One entry of a chunk table: a piece of one tensor, at most chunk_elems long. */
+typedef struct dp_chunk {
+    int64_t flat;    /* flat index of the chunk's first element */
+    int64_t offset;  /* index of that element inside its tensor */
+    int32_t tensor;  /* tensor index */
+    int32_t len;     /* elements */
+} dp_chunk;
+
+typedef struct dp_plan dp_plan;
+
+int dp_abi_version(void);
+const char* dp_status_string(dp_status s);
+/* Message of the calling thread's last failure ("" if none).  Valid until the
+ * thread's next failing call. */
+const char* dp_last_error(void);
+
+/* Builds a plan over a ragged tensor list: prefix sums of the flat space and
+ * the chunk table of [0, P) (host work only; no GPU is touched).  Rejects
+ * negative sizes, bad dtypes, n_replicas outside [1, DP_MAX_REPLICAS] and bad
+ * chunk sizes with DP_ERR_BAD_LAYOUT.  *out receives the plan. */
+dp_status dp_plan_create(const dp_layout* layout, dp_plan** out);
+
+/* Frees the library's device memory (tables, partials, state) and the plan.
+ * Synchronises the device first.  Null is accepted. */
+dp_status dp_plan_destroy(dp_plan* plan);
+
+dp_status dp_plan_info_get(const dp_plan* plan, dp_plan_info* out);
+
+/* Copies entries [first, first + cap) of the chunk table of [begin, end) into
+ * host array out and the table's length into *count (host work only). */
+dp_status dp_plan_chunks(const dp_plan* plan, int64_t begin, int64_t end, int64_t first, int64_t cap,
+                         dp_chunk* out, int64_t* count);
+
+/* Binds one contiguous device buffer to a role: tensor i starts at element
+ * prefix[i] of it.  replica selects the GRAD / ACC buffer (0 for the other
+ * roles).  Host work only; rebinding is cheap and may happen between any two
+ * calls. */
+dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* device_base);
+
+/* Binds one device pointer per tensor (host array ptrs[num_tensors]).  The
+ * pointer table is copied to the device: this call allocates and
+ * synchronises. */
+dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
+
+/* Builds and uploads the chunk table of [begin, end) so later dp_adam_step
+ * calls on that range do not allocate (allocates; synchronises). */
+dp_status dp_plan_prepare_range(dp_plan* plan, int64_t begin, int64_t end);
+
+/* Allocates the device state and statistics scratch on the current device
+ * (first call), and sets t = 0, beta powers = 1, scale = init_scale (1 with
+ * DP_SCALER_NONE), growth tracker 0, asynchronously on stream. */
+dp_status dp_state_init(dp_plan* plan, const dp_state_cfg* cfg, hipStream_t stream);
+
+/* Micro-step accumulation [first page, averaging formula]: over [0, P),
+ * ACC[replica] = GRAD[replica] when first != 0, else ACC[replica] + GRAD[replica],
+ * in binary32.  emit_stats != 0 (only with n_replicas == 1, where g_bar is
+ * ACC[0]) also writes the per-chunk statistics of the result, so the last
+ * micro-step replaces the scan of dp_grad_stats.  DP_ERR_STATE: first == 0 on
+ * a replica with no first micro-step since the last reduction. */
+dp_status dp_accumulate(dp_plan* plan, int32_t replica, int32_t first, int32_t emit_stats, hipStream_t stream);
+
+/* Replica average [first page, averaging formula and reduction-order
+ * paragraph]: GBAR = (sum_r SRC[r]) / n over [0, P) with a fixed pairwise order
+ * (adjacent pairs by levels, an odd last term carried, binary32 partial sums),
+ * and the per-chunk statistics of GBAR.  src is DP_ROLE_ACC (the
+ * accumulators; every replica must have the same number of micro-steps, else
+ * DP_ERR_STATE) or DP_ROLE_GRAD (n low-precision partials, a = 1). */
+dp_status dp_reduce_replicas(dp_plan* plan, dp_role src, hipStream_t stream);
+
+/* Global statistics and per-step scalars.  scan != 0 first reads GBAR to
+ * write the per-chunk statistics; scan == 0 uses those written by
+ * dp_reduce_replicas or dp_accumulate(emit_stats) (DP_ERR_STATE if there are
+ * none).  Then, on the device: norm = sqrt(sum g_bar^2) / scale; if any entry
+ * of g_bar is inf or NaN the step is skipped (iter += 1, a dynamic scale backs
+ * off); otherwise clip = max_norm / norm when max_norm > 0 and norm >
+ * max_norm (else 1), gscale = clip / scale, t += 1, the beta powers advance,
+ * iter += 1, and a dynamic scale grows after growth_interval clean steps.
+ * DP_ERR_STATE before dp_state_init. */
+dp_status dp_grad_stats(dp_plan* plan, int32_t scan, double max_norm, hipStream_t stream);
+
+/* The fused update over [shard_begin, shard_end) [first page,
+ * mixed-precision and ZeRO paragraphs; Adam with bias correction and
+ * decoupled weight decay]: one read of GBAR, MASTER, EXP_AVG, EXP_AVG_SQ and
+ * one write of MASTER, EXP_AVG, EXP_AVG_SQ, PARAM per element:
+ *   g = g_bar * gscale
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *   w = w (1 - lr wd) - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *   p = w rounded to nearest-even in the param dtype
+ * computed in binary64 and stored in binary32.  Nothing is written when the
+ * finalised step was skipped.  Any partition of [0, P) into ranges gives the
+ * same result as one call on [0, P).  DP_ERR_STATE if dp_grad_stats has not
+ * run since the last accumulation or reduction.  The first call on a range
+ * that dp_plan_prepare_range did not prepare allocates its table. */
+dp_status dp_adam_step(dp_plan* plan, const dp_adam_hparams* hp, int64_t shard_begin, int64_t shard_end,
+                       hipStream_t stream);
+
+/* Copies the device scalar state into host struct out after the stream's
+ * previous work (synchronises the stream). */
+dp_status dp_read_state(dp_plan* plan, dp_step_state* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPSTEP_H */

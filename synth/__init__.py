@@ -119,6 +119,7 @@ def _gpu_lib():
     if _gpu is None:
         if not os.path.exists(GPU_LIB_PATH):
             raise ImportError(f"{GPU_LIB_PATH} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (load torch's HIP runtime first: one runtime per process)
         lib = ctypes.CDLL(GPU_LIB_PATH)
         lib.synth_normal_device.restype = ctypes.c_int
         lib.synth_normal_device.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,

@@ -1,0 +1,171 @@
+"""Shared helpers of the GPU parity tests: run a workload through the HIP
+library, run the same workload through the CPU oracle, compare.
+
+Inputs on both sides come from the seeded generators in ``synth`` (device twin
+on the GPU side, host twin on the oracle side); nothing the GPU computes is
+fed to the oracle."""
+from __future__ import annotations
+
+import os
+import sys
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from gradient_reduce_adam_amd import driver
+
+THREADS = int(os.environ.get("DP_ORACLE_THREADS", str(min(16, os.cpu_count() or 8))))
+
+# Tolerances stated for the step: binary32 master, m, v within 2e-6 relative
+# with a 1e-9 absolute floor; the gradient norm within 1e-5 relative;
+# low-precision parameters within 1 ulp; flags and counters exact.
+RTOL_STATE = 2e-6
+ATOL_STATE = 1e-9
+RTOL_NORM = 1e-5
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------
+# GPU side
+# ----------------------------------------------------------------------------
+class GpuRun:
+    """A workload on the GPU: the library's driver plus device-generated inputs."""
+
+    def __init__(self, w, shards=None, chunk_elems: int = 0, grad_slots: Optional[int] = None):
+        self.w = w
+        self.d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
+                               weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
+                               scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
+                               growth_interval=w.growth_interval, partials=w.partials, shards=shards,
+                               chunk_elems=chunk_elems)
+        slots = w.n if w.partials else 1
+        self.slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(slots)]
+        self.stream = self.d.stream.cuda_stream
+        self.d.set_master(lambda ptr: synth.master_device(w, ptr, self.stream))
+        self.states: List[dict] = []
+
+    def produce(self, step: int, r: int, k: int, scale: float) -> int:
+        buf = self.slots[r % len(self.slots)]
+        synth.grad_device(self.w, step, r, k, buf.data_ptr(), scale, self.stream)
+        return buf.data_ptr()
+
+    def step(self) -> dict:
+        s = self.d.step(self.produce, sync_scale=True)
+        self.states.append(s)
+        return s
+
+    def run(self, steps: int) -> List[dict]:
+        for _ in range(steps):
+            self.step()
+        return self.states
+
+    def window(self, lo: int, hi: int) -> Dict[str, np.ndarray]:
+        torch.cuda.synchronize()
+        return {"w": self.d.master[lo:hi].cpu().numpy(), "m": self.d.exp_avg[lo:hi].cpu().numpy(),
+                "v": self.d.exp_avg_sq[lo:hi].cpu().numpy(),
+                "p": self.d.param[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16),
+                "gbar": self.d.gbar[lo:hi].cpu().numpy()}
+
+    def close(self):
+        self.d.close()
+        del self.slots
+        self.d = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# oracle side
+# ----------------------------------------------------------------------------
+def oracle_run(w, steps: int, windows=None, keep_gbar=(), chunk: int = 1 << 20):
+    def grad_fn(step, r, k, lo, hi, scale):
+        return synth.grad_host(w, step, r, k, lo, hi, scale)
+
+    def master_fn(lo, hi):
+        return synth.master_host(w, lo, hi)
+
+    return oracle.run(w, steps, grad_fn, master_fn, windows=windows, threads=THREADS, chunk=chunk,
+                      keep_gbar=keep_gbar)
+
+
+# ----------------------------------------------------------------------------
+# comparison
+# ----------------------------------------------------------------------------
+def ulps32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    ai = a.view(np.int32).astype(np.int64)
+    bi = b.view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+def ulps16(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    ai = a.astype(np.int64)
+    bi = b.astype(np.int64)
+    ai = np.where(ai >= 0x8000, -(ai & 0x7FFF), ai)
+    bi = np.where(bi >= 0x8000, -(bi & 0x7FFF), bi)
+    return np.abs(ai - bi)
+
+
+def assert_state_close(got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], where: str = "") -> dict:
+    report = {}
+    for key in ("w", "m", "v"):
+        g, r = got[key], ref[key]
+        assert g.shape == r.shape, (key, g.shape, r.shape)
+        err = np.abs(g.astype(np.float64) - r.astype(np.float64))
+        lim = RTOL_STATE * np.abs(r.astype(np.float64)) + ATOL_STATE
+        bad = np.flatnonzero(err > lim)
+        report[key + "_max_ulp"] = int(ulps32(g, r).max()) if g.size else 0
+        assert bad.size == 0, f"{where} {key}: {bad.size} elements out of tolerance, first at {bad[:5]}: " \
+                              f"gpu {g[bad[:5]]} oracle {r[bad[:5]]}"
+    pu = ulps16(got["p"], ref["p"])
+    report["p_max_ulp"] = int(pu.max()) if pu.size else 0
+    assert report["p_max_ulp"] <= 1, f"{where} params differ by {report['p_max_ulp']} ulp"
+    return report
+
+
+def assert_scalars_match(gpu: dict, ref: dict, where: str = "") -> None:
+    for k in ("t", "iter", "found_inf", "growth_tracker", "scale"):
+        assert gpu[k] == ref[k], f"{where} {k}: gpu {gpu[k]} oracle {ref[k]}"
+    for k in ("beta1_pow", "beta2_pow"):
+        assert gpu[k] == ref[k], f"{where} {k}: gpu {gpu[k]!r} oracle {ref[k]!r}"
+    if np.isfinite(ref["norm"]):
+        assert abs(gpu["norm"] - ref["norm"]) <= RTOL_NORM * abs(ref["norm"]), (where, gpu["norm"], ref["norm"])
+        assert abs(gpu["clip"] - ref["clip"]) <= RTOL_NORM * abs(ref["clip"]), (where, gpu["clip"], ref["clip"])
+    else:
+        assert not np.isfinite(gpu["norm"])
+
+
+def sample_windows(w, count: int = 24, width: int = 4096, seed: int = 0) -> List[Tuple[int, int]]:
+    """First and last elements, windows straddling tensor boundaries and
+    chunk boundaries, around each injected element, and seeded random ones."""
+    P = w.P
+    rng = np.random.default_rng(seed)
+    wins = [(0, min(P, width)), (max(0, P - width), P)]
+    off = w.offsets
+    for t in range(1, min(w.T, 40)):
+        c = int(off[t])
+        wins.append((max(0, c - 128), min(P, c + 128)))
+    for c in (65536, 3 * 65536, P // 2 // 65536 * 65536):
+        if 0 < c < P:
+            wins.append((max(0, c - 64), min(P, c + 64)))
+    for (_, _, _, idx, _) in w.injections:
+        wins.append((max(0, idx - 256), min(P, idx + 256)))
+    for _ in range(count):
+        lo = int(rng.integers(0, max(1, P - width)))
+        wins.append((lo, min(P, lo + width)))
+    wins = sorted(set(wins))
+    merged: List[Tuple[int, int]] = []
+    for lo, hi in wins:
+        if merged and lo <= merged[-1][1]:
+            merged[-1] = (merged[-1][0], max(hi, merged[-1][1]))
+        else:
+            merged.append((lo, hi))
+    return merged

@@ -1,0 +1,157 @@
+"""The C-ABI library on the host: it loads, exports every symbol its header
+declares, and its host-side logic (layout checks, chunk tables, byte model,
+argument and ordering errors) behaves as documented.  No compute call is made
+here: everything below fails validation before touching a GPU, or is host
+work by contract."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dpstep.h")
+
+dp = pytest.importorskip("gradient_reduce_adam_amd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(dp_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 16, names
+    assert sorted(dp.EXPORTS) == names
+    for n in names:
+        assert hasattr(dp.lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert dp.dp_abi_version() == 1
+    assert dp.dp_status_string(dp.DP_ERR_RANGE) == "range out of bounds"
+    assert dp.dp_status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("kw", [dict(n_replicas=0), dict(n_replicas=17), dict(grad_dtype="f32"),
+                                dict(param_dtype="f32"), dict(chunk_elems=100), dict(chunk_elems=1 << 27)])
+def test_bad_layouts_rejected(kw):
+    args = dict(numel=[10, 20], n_replicas=2, grad_dtype="bf16", param_dtype="bf16", chunk_elems=0)
+    args.update(kw)
+    with pytest.raises(dp.DpError) as e:
+        dp.dp_plan_create(**args)
+    assert e.value.status == dp.DP_ERR_BAD_LAYOUT
+
+
+def test_negative_numel_rejected():
+    with pytest.raises(dp.DpError) as e:
+        dp.dp_plan_create([5, -1], 1, "bf16", "bf16")
+    assert e.value.status == dp.DP_ERR_BAD_LAYOUT and "numel[1]" in e.value.message
+
+
+def _brute_chunks(numel, chunk, begin, end):
+    out = []
+    pos = 0
+    for t, n in enumerate(numel):
+        for off in range(0, n, chunk):
+            lo, hi = pos + off, pos + min(n, off + chunk)
+            a, b = max(lo, begin), min(hi, end)
+            if a < b:
+                out.append((a, a - pos, t, b - a))
+        pos += n
+    return out
+
+
+@pytest.mark.parametrize("numel,chunk", [((1000, 0, 3, 70000, 256, 65536, 65537), 256),
+                                         ((1 << 20,), 65536), ((5, 5, 5), 256), ((), 256)])
+def test_chunk_table_matches_brute_force(numel, chunk):
+    with dp.Plan(numel, 1, "bf16", "bf16", chunk) as p:
+        P = sum(numel)
+        rng = np.random.default_rng(3)
+        ranges = [(0, P), (0, 0)] + [tuple(sorted(rng.integers(0, P + 1, 2))) for _ in range(20)] if P else [(0, 0)]
+        for b, e in ranges:
+            got = p.chunks(int(b), int(e))
+            ref = _brute_chunks(numel, chunk, int(b), int(e))
+            assert [tuple(int(x) for x in r) for r in got] == ref
+
+
+def test_chunk_table_of_a_2pow32_tensor_uses_64bit_indices():
+    with dp.Plan((1 << 32, 7), 4, "f16", "f16") as p:
+        c = p.chunks()
+        assert len(c) == (1 << 32) // 65536 + 1
+        assert int(c[-2]["flat"]) == (1 << 32) - 65536 and int(c[-1]["flat"]) == 1 << 32
+        assert int(c[-1]["offset"]) == 0 and int(c[-1]["tensor"]) == 1 and int(c[-1]["len"]) == 7
+        mid = p.chunks((1 << 31) + 5, (1 << 31) + 70000)
+        assert int(mid[0]["offset"]) == (1 << 31) + 5 and int(mid[0]["len"]) == 65531
+
+
+def test_plan_info_byte_model():
+    numel = (50257 * 768, 768, 3)
+    with dp.Plan(numel, 8, "bf16", "bf16") as p:
+        info = p.info()
+        P = sum(numel)
+        assert info["params"] == P and info["num_tensors"] == 3 and info["n_replicas"] == 8
+        assert info["state_bytes"] == 16 * P
+        assert info["bytes_accumulate_first"] == 6 * P and info["bytes_accumulate"] == 10 * P
+        assert info["bytes_reduce_acc"] == (4 * 8 + 4) * P and info["bytes_reduce_partials"] == (2 * 8 + 4) * P
+        assert info["bytes_adam"] == 30 * P and info["bytes_stats_scan"] == 4 * P
+        assert info["num_chunks"] == len(p.chunks())
+
+
+def test_bind_and_call_errors_before_any_launch():
+    with dp.Plan((1000, 24), 2, "bf16", "bf16") as p:
+        h = p.handle
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_plan_bind_flat(h, 9, 0, 0x1000)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_ACC, 2, 0x1000)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_MASTER, 1, 0x1000)  # only GRAD / ACC are per replica
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate(h, 0, True, stream=0)
+        assert e.value.status == dp.DP_ERR_UNBOUND
+        dp.dp_plan_bind_flat(h, dp.DP_ROLE_GRAD, 0, 0x1000)
+        dp.dp_plan_bind_flat(h, dp.DP_ROLE_ACC, 0, 0x2000)
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate(h, 0, False, stream=0)  # no first micro-step yet
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate(h, 0, True, emit_stats=True, stream=0)  # n = 2
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate(h, 2, True, stream=0)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_grad_stats(h, False, 1.0, stream=0)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_replicas(h, dp.DP_ROLE_ACC, stream=0)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_replicas(h, dp.DP_ROLE_MASTER, stream=0)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        for b, e_ in ((-1, 10), (5, 4), (0, 1025)):
+            with pytest.raises(dp.DpError) as e:
+                dp.dp_adam_step(h, 1e-3, 1e-8, 0.0, b, e_, stream=0)
+            assert e.value.status == dp.DP_ERR_RANGE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_adam_step(h, 1e-3, 0.0, 0.0, 0, 10, stream=0)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_adam_step(h, 1e-3, 1e-8, 0.0, 0, 10, stream=0)  # no statistics yet
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_read_state(h, stream=0)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_plan_chunks(h, 0, 2000)
+        assert e.value.status == dp.DP_ERR_RANGE
+        assert "not inside" in dp.dp_last_error()
+
+
+def test_destroy_null_is_ok():
+    dp.dp_plan_destroy(0)
