@@ -40,6 +40,7 @@ def parse():
                     help="tiny | gpt2_small | zero3_rank_7b | unsharded_7b | tp_column_slice")
     ap.add_argument("--cpu-sample", type=int, default=1 << 22, help="params in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
     return ap.parse_args()
 
 
@@ -49,36 +50,29 @@ def kernel_source_hash() -> str:
 
 
 def bytes_model(w) -> dict:
-    """Algorithmic HBM bytes per parameter of each call kind in one step."""
-    sg = 2.0
-    sp = 2.0
+    """Algorithmic HBM bytes per parameter of each call kind in one step of
+    the fused sequence: micro-steps 1 .. a-1 of every replica per launch, the
+    last micro-step fused with the replica average, then the update."""
+    sg, sp = 2.0, 2.0
     per = {}
-    if w.partials:
-        per["reduce"] = w.n * sg + 4.0
-    else:
+    last = 1 if w.partials else w.a
+    if last >= 2:
         per["accumulate_first"] = w.n * (sg + 4.0)
-        per["accumulate"] = w.n * (w.a - 1) * (sg + 8.0)
-        if w.n > 1:
-            per["reduce"] = 4.0 * w.n + 4.0
+    if last >= 3:
+        per["accumulate"] = w.n * (last - 2) * (sg + 8.0)
+    per["accumulate_reduce"] = w.n * (sg + (4.0 if last >= 2 else 0.0)) + 4.0
     per["adamw"] = 16.0 + 12.0 + sp
     return per
 
 
 def launch_bytes(w, kind: str) -> float:
     """Algorithmic bytes of one launch of `kind` over the whole flat space."""
-    P = float(w.P)
-    if kind == "accumulate_first":
-        return P * (2.0 + 4.0)
-    if kind == "accumulate":
-        return P * (2.0 + 8.0)
-    if kind == "reduce":
-        return P * ((2.0 * w.n if w.partials else 4.0 * w.n) + 4.0)
-    if kind == "adamw":
-        return P * 30.0
-    return 0.0
+    per = bytes_model(w)
+    launches = {"accumulate": max(1, (1 if w.partials else w.a) - 2)}
+    return w.P * per[kind] / launches.get(kind, 1)
 
 
-def run_gpu(w, steps: int, warmup: int):
+def run_gpu(w, steps: int, warmup: int, chunk: int = 0):
     import torch
 
     import synth
@@ -88,7 +82,7 @@ def run_gpu(w, steps: int, warmup: int):
     d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
-                      growth_interval=w.growth_interval, partials=w.partials)
+                      growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -96,10 +90,10 @@ def run_gpu(w, steps: int, warmup: int):
     # one batch of gradients, resident before the timed region
     calls = [(r, 1) for r in range(w.n)] if w.partials else [(r, k) for k in range(1, w.a + 1) for r in range(w.n)]
     per_buf = 2 * w.P
-    nbuf = len(calls) if len(calls) * per_buf <= RESIDENT_GRAD_BUDGET else max(2 if not w.partials else w.n,
-                                                                               int(RESIDENT_GRAD_BUDGET // per_buf))
-    if w.partials:
-        nbuf = max(nbuf, w.n)
+    # a ring of distinct buffers; a micro-step's n replicas (and consecutive
+    # launches) never share one, and every buffer is far larger than the caches
+    nbuf = len(calls) if len(calls) * per_buf <= RESIDENT_GRAD_BUDGET else int(RESIDENT_GRAD_BUDGET // per_buf)
+    nbuf = max(nbuf, 2 * w.n if not w.partials else w.n)
     bufs = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(nbuf)]
     addr = {}
     for i, (r, k) in enumerate(calls):
@@ -125,20 +119,15 @@ def run_gpu(w, steps: int, warmup: int):
 
     def one_step(rec: bool):
         h = plan.handle
-        if w.partials:
+        last = 1 if w.partials else w.a
+        for k in range(1, last):
             for r in range(w.n):
-                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, 1)])
-            timed("reduce", lambda: plan.reduce_replicas("grad", stream=stream), rec)
-        else:
-            for k in range(1, w.a + 1):
-                for r in range(w.n):
-                    dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, k)])
-                    kind = "accumulate_first" if k == 1 else "accumulate"
-                    timed(kind, lambda r=r, k=k: plan.accumulate(r, first=(k == 1),
-                                                                 emit_stats=(w.n == 1 and k == w.a),
-                                                                 stream=stream), rec)
-            if w.n > 1:
-                timed("reduce", lambda: plan.reduce_replicas("acc", stream=stream), rec)
+                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, k)])
+            timed("accumulate_first" if k == 1 else "accumulate",
+                  lambda k=k: plan.accumulate_all(first=(k == 1), stream=stream), rec)
+        for r in range(w.n):
+            dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, last)])
+        timed("accumulate_reduce", lambda: plan.accumulate_reduce(stream=stream), rec)
         timed("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream), rec)
         timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
 
@@ -197,7 +186,7 @@ def main():
     from synth import workloads
 
     w = workloads.by_name(args.workload)
-    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup)
+    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w)
     step_bytes = sum(per_param.values()) * w.P
@@ -232,7 +221,8 @@ def main():
         "config": {"workload": w.name, "params": w.P, "tensors": w.T, "n_replicas": w.n, "micro_steps": w.a,
                    "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "state": "fp32 master/m/v",
                    "update_arithmetic": "f64", "clip": w.max_norm, "loss_scale": w.scaler,
-                   "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)"},
+                   "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)",
+                   "chunk_elems": args.chunk or 2048},
         "hbm_gbps": hbm_gbps,
         "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
         "bytes_per_param_step": sum(per_param.values()),

@@ -28,7 +28,7 @@ DP_F32, DP_F16, DP_BF16 = 0, 1, 2
  DP_ROLE_GBAR) = range(7)
 DP_SCALER_NONE, DP_SCALER_STATIC, DP_SCALER_DYNAMIC = 0, 1, 2
 DP_MAX_REPLICAS = 16
-DP_DEFAULT_CHUNK = 65536
+DP_DEFAULT_CHUNK = 2048
 
 DTYPES = {"f32": DP_F32, "f16": DP_F16, "bf16": DP_BF16}
 SCALERS = {"none": DP_SCALER_NONE, "static": DP_SCALER_STATIC, "dynamic": DP_SCALER_DYNAMIC}
@@ -38,8 +38,8 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 # every exported symbol of dpstep.h
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
-           "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_reduce_replicas", "dp_grad_stats",
-           "dp_adam_step", "dp_read_state")
+           "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
+           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_read_state")
 
 
 class Layout(ctypes.Structure):
@@ -73,7 +73,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_replicas", ctypes.c_int32), ("chunk_elems", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("state_bytes", ctypes.c_double), ("bytes_accumulate_first", ctypes.c_double),
                 ("bytes_accumulate", ctypes.c_double), ("bytes_reduce_acc", ctypes.c_double),
-                ("bytes_reduce_partials", ctypes.c_double), ("bytes_stats_scan", ctypes.c_double),
+                ("bytes_reduce_partials", ctypes.c_double), ("bytes_accumulate_reduce", ctypes.c_double),
+                ("bytes_stats_scan", ctypes.c_double),
                 ("bytes_adam", ctypes.c_double)]
 
     def as_dict(self) -> dict:
@@ -139,6 +140,8 @@ def _load():
         "dp_plan_prepare_range": (ctypes.c_int, [vp, i64, i64]),
         "dp_state_init": (ctypes.c_int, [vp, ctypes.POINTER(StateCfg), vp]),
         "dp_accumulate": (ctypes.c_int, [vp, i32, i32, i32, vp]),
+        "dp_accumulate_all": (ctypes.c_int, [vp, i32, vp]),
+        "dp_accumulate_reduce": (ctypes.c_int, [vp, vp]),
         "dp_reduce_replicas": (ctypes.c_int, [vp, ctypes.c_int, vp]),
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
@@ -245,6 +248,14 @@ def dp_accumulate(plan: int, replica: int, first: bool, emit_stats: bool = False
                              ctypes.c_void_p(_stream(stream))))
 
 
+def dp_accumulate_all(plan: int, first: bool, stream=None) -> None:
+    _check(lib.dp_accumulate_all(ctypes.c_void_p(plan), int(bool(first)), ctypes.c_void_p(_stream(stream))))
+
+
+def dp_accumulate_reduce(plan: int, stream=None) -> None:
+    _check(lib.dp_accumulate_reduce(ctypes.c_void_p(plan), ctypes.c_void_p(_stream(stream))))
+
+
 def dp_reduce_replicas(plan: int, src: int = DP_ROLE_ACC, stream=None) -> None:
     _check(lib.dp_reduce_replicas(ctypes.c_void_p(plan), src, ctypes.c_void_p(_stream(stream))))
 
@@ -319,6 +330,12 @@ class Plan:
 
     def accumulate(self, replica: int, first: bool, emit_stats: bool = False, stream=None) -> None:
         dp_accumulate(self.handle, replica, first, emit_stats, stream)
+
+    def accumulate_all(self, first: bool, stream=None) -> None:
+        dp_accumulate_all(self.handle, first, stream)
+
+    def accumulate_reduce(self, stream=None) -> None:
+        dp_accumulate_reduce(self.handle, stream)
 
     def reduce_replicas(self, src: str = "acc", stream=None) -> None:
         dp_reduce_replicas(self.handle, ROLES[src], stream)

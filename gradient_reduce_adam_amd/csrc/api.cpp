@@ -64,6 +64,7 @@ struct dp_plan {
     int device = -1;
     dpk::DevState* state = nullptr;
     dpk::StatsBuf stats{nullptr, nullptr};
+    dpk::FoldBuf fold{nullptr, nullptr};
     DeviceTable full;
     std::vector<DeviceTable> ranges;
 
@@ -246,6 +247,8 @@ dp_status dp_plan_destroy(dp_plan* p) {
         if (p->state) (void)hipFree(p->state);
         if (p->stats.sumsq) (void)hipFree(p->stats.sumsq);
         if (p->stats.bad) (void)hipFree(p->stats.bad);
+        if (p->fold.sumsq) (void)hipFree(p->fold.sumsq);
+        if (p->fold.bad) (void)hipFree(p->fold.bad);
     }
     delete p;
     return DP_OK;
@@ -268,6 +271,7 @@ dp_status dp_plan_info_get(const dp_plan* p, dp_plan_info* out) {
     out->bytes_accumulate = P * (sg + 8.0);
     out->bytes_reduce_acc = P * (4.0 * p->n + 4.0);
     out->bytes_reduce_partials = P * (sg * p->n + 4.0);
+    out->bytes_accumulate_reduce = P * ((sg + 4.0) * p->n + 4.0);
     out->bytes_stats_scan = P * 4.0;
     out->bytes_adam = P * (16.0 + 12.0 + sp);
     return DP_OK;
@@ -366,6 +370,11 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
+        const size_t ng = (np + dpk::kFoldGroup - 1) / dpk::kFoldGroup;
+        e = hipMalloc(reinterpret_cast<void**>(&p->fold.sumsq), ng * sizeof(double));
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics groups: %s", hipGetErrorString(e));
+        e = hipMalloc(reinterpret_cast<void**>(&p->fold.bad), ng * sizeof(uint64_t));
+        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics groups: %s", hipGetErrorString(e));
     }
     const double scale = cfg->scaler_mode == DP_SCALER_NONE ? 1.0 : cfg->init_scale;
     s = check_launch(dpk::launch_state_init(p->state, scale, stream), "state init launch");
@@ -410,30 +419,25 @@ dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit
     return DP_OK;
 }
 
-dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
-    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_replicas: null plan");
-    if (src != DP_ROLE_ACC && src != DP_ROLE_GRAD)
-        return fail(DP_ERR_INVALID_ARG, "src must be DP_ROLE_ACC or DP_ROLE_GRAD");
-    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_replicas before dp_state_init");
-    dpk::Srcs srcs{};
+static dp_status bound_replicas(dp_plan* p, dp_role role, dpk::Srcs* out) {
     for (int32_t r = 0; r < p->n; ++r) {
-        const Binding& b = p->roles[src][r];
-        if (!b.bound) return fail(DP_ERR_UNBOUND, "role %s of replica %d is not bound", src == DP_ROLE_ACC ? "ACC" : "GRAD", r);
-        srcs.r[r] = b.ref();
+        const Binding& b = p->roles[role][r];
+        if (!b.bound)
+            return fail(DP_ERR_UNBOUND, "role %s of replica %d is not bound", role == DP_ROLE_ACC ? "ACC" : "GRAD", r);
+        out->r[r] = b.ref();
     }
-    if (src == DP_ROLE_ACC) {
-        for (int32_t r = 0; r < p->n; ++r)
-            if (p->micro[r] != p->micro[0] || p->micro[r] == 0)
-                return fail(DP_ERR_STATE, "replicas accumulated different numbers of micro-steps (replica %d: %d, replica 0: %d)",
-                            r, p->micro[r], p->micro[0]);
-    }
+    return DP_OK;
+}
+
+static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs& accs, const dpk::Srcs& grads,
+                               hipStream_t stream) {
     const Binding* gb = gbar_binding(p);
     if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
     dp_status s = ensure_full(p);
     if (s != DP_OK) return s;
     if (p->full.count > 0) {
-        s = check_launch(dpk::launch_reduce(src == DP_ROLE_ACC ? DP_F32 : p->gdt, p->n, p->full.dev, p->full.count, srcs,
-                                            gb->ref(), p->stats, stream),
+        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, p->full.dev, p->full.count, accs, grads, gb->ref(),
+                                            p->stats, stream),
                          "reduce launch");
         if (s != DP_OK) return s;
     }
@@ -441,6 +445,70 @@ dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
     p->partials_valid = true;
     p->stats_current = false;
     return DP_OK;
+}
+
+dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_replicas: null plan");
+    if (src != DP_ROLE_ACC && src != DP_ROLE_GRAD)
+        return fail(DP_ERR_INVALID_ARG, "src must be DP_ROLE_ACC or DP_ROLE_GRAD");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_replicas before dp_state_init");
+    dpk::Srcs accs{}, grads{};
+    dp_status s = bound_replicas(p, src, src == DP_ROLE_ACC ? &accs : &grads);
+    if (s != DP_OK) return s;
+    if (src == DP_ROLE_ACC) {
+        for (int32_t r = 0; r < p->n; ++r)
+            if (p->micro[r] != p->micro[0] || p->micro[r] == 0)
+                return fail(DP_ERR_STATE, "replicas accumulated different numbers of micro-steps (replica %d: %d, replica 0: %d)",
+                            r, p->micro[r], p->micro[0]);
+    }
+    return reduce_common(p, src == DP_ROLE_ACC ? dpk::ReduceMode::kAccumulators : dpk::ReduceMode::kGradients, accs,
+                         grads, stream);
+}
+
+dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_all: null plan");
+    dpk::Srcs grads{}, accs{};
+    dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+    if (s == DP_OK) s = bound_replicas(p, DP_ROLE_ACC, &accs);
+    if (s != DP_OK) return s;
+    for (int32_t r = 0; r < p->n; ++r) {
+        if (!first && p->micro[r] == 0)
+            return fail(DP_ERR_STATE, "replica %d: first == 0 without a first micro-step since the last reduction", r);
+        if (p->micro[r] != p->micro[0])
+            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
+                        p->micro[r], p->micro[0]);
+    }
+    s = ensure_full(p);
+    if (s != DP_OK) return s;
+    if (p->full.count > 0) {
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.dev, p->full.count, grads, accs,
+                                                    stream),
+                         "accumulate launch");
+        if (s != DP_OK) return s;
+    }
+    for (int32_t r = 0; r < p->n; ++r) p->micro[r] = first ? 1 : p->micro[r] + 1;
+    p->stats_current = false;
+    p->partials_valid = false;
+    return DP_OK;
+}
+
+dp_status dp_accumulate_reduce(dp_plan* p, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce: null plan");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce before dp_state_init");
+    dpk::Srcs grads{}, accs{};
+    dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+    if (s != DP_OK) return s;
+    for (int32_t r = 0; r < p->n; ++r)
+        if (p->micro[r] != p->micro[0])
+            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
+                        p->micro[r], p->micro[0]);
+    const bool with_acc = p->micro[0] > 0;
+    if (with_acc) {
+        s = bound_replicas(p, DP_ROLE_ACC, &accs);
+        if (s != DP_OK) return s;
+    }
+    return reduce_common(p, with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients, accs, grads,
+                         stream);
 }
 
 dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t stream) {
@@ -462,7 +530,7 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
     }
     dpk::ScalerArgs a{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, max_norm,
                       p->cfg.scaler_mode, p->cfg.growth_interval};
-    s = check_launch(dpk::launch_finalize(p->stats, p->full.count, p->state, a, stream), "finalize launch");
+    s = check_launch(dpk::launch_finalize(p->stats, p->full.count, p->fold, p->state, a, stream), "finalize launch");
     if (s != DP_OK) return s;
     p->partials_valid = false;
     p->stats_current = true;

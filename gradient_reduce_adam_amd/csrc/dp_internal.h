@@ -40,6 +40,14 @@ struct StatsBuf {
     uint32_t* bad;
 };
 
+// Second level of the statistics fold: one entry per group of kFoldGroup
+// chunk partials (used when a table has more than kFoldGroup chunks).
+constexpr int64_t kFoldGroup = 4096;
+struct FoldBuf {
+    double* sumsq;
+    uint64_t* bad;
+};
+
 struct AdamArgs {
     double lr, eps, weight_decay, beta1, beta2;
 };
@@ -51,10 +59,20 @@ struct ScalerArgs {
 
 hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const dp_chunk* chunks, int64_t nchunks,
                              RoleRef grad, RoleRef acc, StatsBuf sb, hipStream_t stream);
-hipError_t launch_reduce(dp_dtype src_dt, int n, const dp_chunk* chunks, int64_t nchunks, const Srcs& srcs,
-                         RoleRef gbar, StatsBuf sb, hipStream_t stream);
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const dp_chunk* chunks, int64_t nchunks,
+                                 const Srcs& grads, const Srcs& accs, hipStream_t stream);
+
+// What each replica contributes to the reduction.
+enum class ReduceMode {
+    kAccumulators,  // acc_r (binary32)
+    kGradients,     // g_r (the gradient dtype): partials, or a single micro-step
+    kAccPlusGrad    // acc_r + g_r: the last micro-step fused, acc_r not written back
+};
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const dp_chunk* chunks, int64_t nchunks,
+                         const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_stats(const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, StatsBuf sb, hipStream_t stream);
-hipError_t launch_finalize(StatsBuf sb, int64_t nparts, DevState* st, const ScalerArgs& args, hipStream_t stream);
+hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
+                           hipStream_t stream);
 hipError_t launch_adamw(dp_dtype pdt, const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, RoleRef w, RoleRef m,
                         RoleRef v, RoleRef p, const DevState* st, const AdamArgs& args, hipStream_t stream);
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t stream);

@@ -125,27 +125,26 @@ __device__ __forceinline__ float tree_sum(float (&b)[N]) {
     return b[0];
 }
 
-__device__ __forceinline__ float average(float s, float inv_n, double n_d) {
-    // n a power of two: the reciprocal is exact and so is the product.
-    // Otherwise one binary64 division, rounded once to binary32.
-    return inv_n != 0.0f ? s * inv_n : static_cast<float>(static_cast<double>(s) / n_d);
+// Division by n, rounded once to binary32: for n a power of two the binary32
+// reciprocal is exact and so is the product; otherwise one binary64 division
+// (binary64 then binary32 is correctly rounded: 53 >= 2 * 24 + 2).
+template <int N>
+__device__ __forceinline__ float average(float s) {
+    if constexpr ((N & (N - 1)) == 0) return s * (1.0f / static_cast<float>(N));
+    else return static_cast<float>(static_cast<double>(s) / static_cast<double>(N));
 }
 
 // ============================================================================
 // micro-step accumulation: acc = g (first) or acc + g
 // ============================================================================
 template <int kGrad, bool kFirst, bool kStats>
-__global__ void __launch_bounds__(kBlock) k_accumulate(const dp_chunk* __restrict__ chunks, int64_t base,
-                                                         RoleRef grad, RoleRef acc, StatsBuf sb) {
-    const int64_t cid = base + blockIdx.x;
-    const dp_chunk c = chunks[cid];
+__device__ __forceinline__ void accumulate_chunk(const dp_chunk& c, RoleRef grad, RoleRef acc, double& ss,
+                                                 uint32_t& bad) {
     const uint16_t* __restrict__ g = elem_ptr<const uint16_t>(grad, c);
     float* __restrict__ a = elem_ptr<float>(acc, c);
     const int len = c.len, tid = threadIdx.x;
-    double ss = 0.0;
-    uint32_t bad = 0;
     const int nvec = (aligned16(g) && aligned16(a)) ? (len >> 3) : 0;  // 8 elements per vector
-    constexpr int U = 4;
+    constexpr int U = 2;
     for (int v0 = 0; v0 < nvec; v0 += kBlock * U) {
         u32x4 gq[U];
         f32x4 a0[U], a1[U];
@@ -197,68 +196,150 @@ __global__ void __launch_bounds__(kBlock) k_accumulate(const dp_chunk* __restric
             bad += nonfinite(r);
         }
     }
+}
+
+// one replica; with kStats the chunk statistics of the result (n = 1: it is g_bar)
+template <int kGrad, bool kFirst, bool kStats>
+__global__ void __launch_bounds__(kBlock) k_accumulate(const dp_chunk* __restrict__ chunks, int64_t base,
+                                                         RoleRef grad, RoleRef acc, StatsBuf sb) {
+    const int64_t cid = base + blockIdx.x;
+    const dp_chunk c = chunks[cid];
+    double ss = 0.0;
+    uint32_t bad = 0;
+    accumulate_chunk<kGrad, kFirst, kStats>(c, grad, acc, ss, bad);
     if constexpr (kStats) block_stats_store(ss, bad, cid, sb);
 }
 
+// every replica's micro-step in one launch: workgroup b handles replica
+// b / nchunks, chunk b % nchunks (replica-major, so each replica's buffers are
+// streamed in order)
+template <int kGrad, bool kFirst>
+__global__ void __launch_bounds__(kBlock) k_accumulate_all(const dp_chunk* __restrict__ chunks, int64_t nchunks,
+                                                             int64_t base, Srcs grads, Srcs accs) {
+    const int64_t b = base + blockIdx.x;
+    const int r = static_cast<int>(b / nchunks);
+    const dp_chunk c = chunks[b - static_cast<int64_t>(r) * nchunks];
+    double ss = 0.0;
+    uint32_t bad = 0;
+    accumulate_chunk<kGrad, kFirst, false>(c, grads.r[r], accs.r[r], ss, bad);
+}
+
 // ============================================================================
-// replica reduction: gbar = tree(src_0..src_{N-1}) / N, plus chunk statistics
-// kSrc: 0 = binary32 accumulators, 1 / 2 = binary16 / bfloat16 partials
+// replica reduction: gbar = tree(x_0..x_{N-1}) / N, plus chunk statistics
+//   kMode 0: x_r = acc_r                 (binary32 accumulators)
+//   kMode 1: x_r = g_r                   (low-precision gradients or partials)
+//   kMode 2: x_r = acc_r + g_r           (the last micro-step fused: acc_r is
+//                                         not written back)
+// Modes 0 and 2 move 4 elements per lane (one dwordx4 of each binary32
+// stream, a wave reads 1 KiB contiguous); mode 1 moves 8.
 // ============================================================================
-template <int kSrc, int N>
-__global__ void __launch_bounds__(kBlock) k_reduce(const dp_chunk* __restrict__ chunks, int64_t base, Srcs srcs,
-                                                     RoleRef gbar, float inv_n, double n_d, StatsBuf sb) {
+template <int N>
+__device__ __forceinline__ void reduce_store(float (&x)[4][N], float* out, int64_t q, double& ss, uint32_t& bad) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        y[e] = average<N>(tree_sum<N>(x[e]));
+        ss += static_cast<double>(y[e]) * static_cast<double>(y[e]);
+        bad += nonfinite(y[e]);
+    }
+    stg_nt<f32x4>(out, q, f32x4{y[0], y[1], y[2], y[3]});
+}
+
+template <int kind>
+__device__ __forceinline__ f32x4 widen4(u32x2 q) {
+    if constexpr (kind == 2) {
+        return f32x4{__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
+                     __uint_as_float(q.y & 0xFFFF0000u)};
+    } else {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        return __builtin_convertvector(__builtin_bit_cast(f16x4, q), f32x4);
+    }
+}
+
+template <int kMode, int kGrad, int N>
+__global__ void __launch_bounds__(kBlock) k_reduce(const dp_chunk* __restrict__ chunks, int64_t base, Srcs accs,
+                                                     Srcs grads, RoleRef gbar, StatsBuf sb) {
     const int64_t cid = base + blockIdx.x;
     const dp_chunk c = chunks[cid];
     const int len = c.len, tid = threadIdx.x;
-    const void* sp[N];
+    const float* ap[N];
+    const uint16_t* gp[N];
     bool ok = true;
 #pragma unroll
     for (int r = 0; r < N; ++r) {
-        sp[r] = kSrc == 0 ? static_cast<const void*>(elem_ptr<const float>(srcs.r[r], c))
-                          : static_cast<const void*>(elem_ptr<const uint16_t>(srcs.r[r], c));
-        ok = ok && aligned16(sp[r]);
+        if constexpr (kMode != 1) {
+            ap[r] = elem_ptr<const float>(accs.r[r], c);
+            ok = ok && aligned16(ap[r]);
+        }
+        if constexpr (kMode != 0) {
+            gp[r] = elem_ptr<const uint16_t>(grads.r[r], c);
+            ok = ok && (reinterpret_cast<uintptr_t>(gp[r]) & (kMode == 1 ? 15u : 7u)) == 0;
+        }
     }
     float* __restrict__ out = elem_ptr<float>(gbar, c);
     ok = ok && aligned16(out);
-    const int nvec = ok ? (len >> 3) : 0;
+    constexpr int kVec = kMode == 1 ? 8 : 4;  // elements per lane and iteration
+    constexpr int U = ((kMode == 0 && N <= 8) || (kMode == 2 && N <= 4)) ? 2 : 1;
+    const int nvec = ok ? len / kVec : 0;
     double ss = 0.0;
     uint32_t bad = 0;
-    for (int v = tid; v < nvec; v += kBlock) {
-        float x[8][N];
+    for (int v0 = 0; v0 < nvec; v0 += kBlock * U) {
+        if constexpr (kMode != 1) {
+            f32x4 q[U][N];
+            u32x2 h[U][N];
 #pragma unroll
-        for (int r = 0; r < N; ++r) {
-            if constexpr (kSrc == 0) {
-                const f32x4 lo = ldg_nt<f32x4>(sp[r], 2 * v);
-                const f32x4 hi = ldg_nt<f32x4>(sp[r], 2 * v + 1);
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * kBlock + tid;
+                if (v < nvec) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e][r] = lo[e];
-                    x[e + 4][r] = hi[e];
+                    for (int r = 0; r < N; ++r) {
+                        q[u][r] = ldg_nt<f32x4>(ap[r], v);
+                        if constexpr (kMode == 2) h[u][r] = ldg_nt<u32x2>(gp[r], v);
+                    }
                 }
-            } else {
-                const f32x8 f = widen8<kSrc>(ldg_nt<u32x4>(sp[r], v));
+            }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e][r] = f[e];
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * kBlock + tid;
+                if (v < nvec) {
+                    float x[4][N];
+#pragma unroll
+                    for (int r = 0; r < N; ++r) {
+                        f32x4 t = q[u][r];
+                        if constexpr (kMode == 2) t = t + widen4<kGrad>(h[u][r]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e][r] = t[e];
+                    }
+                    reduce_store<N>(x, out, v, ss, bad);
+                }
+            }
+        } else {
+            const int v = v0 + tid;
+            if (v < nvec) {
+                f32x8 f[N];
+#pragma unroll
+                for (int r = 0; r < N; ++r) f[r] = widen8<kGrad>(ldg_nt<u32x4>(gp[r], v));
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float x[4][N];
+#pragma unroll
+                    for (int r = 0; r < N; ++r)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e][r] = f[r][4 * hh + e];
+                    reduce_store<N>(x, out, 2 * static_cast<int64_t>(v) + hh, ss, bad);
+                }
             }
         }
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            y[e] = average(tree_sum<N>(x[e]), inv_n, n_d);
-            ss += static_cast<double>(y[e]) * static_cast<double>(y[e]);
-            bad += nonfinite(y[e]);
-        }
-        stg<f32x4>(out, 2 * v, f32x4{y[0], y[1], y[2], y[3]});
-        stg<f32x4>(out, 2 * v + 1, f32x4{y[4], y[5], y[6], y[7]});
     }
-    for (int i = nvec * 8 + tid; i < len; i += kBlock) {
+    for (int i = nvec * kVec + tid; i < len; i += kBlock) {
         float x[N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            if constexpr (kSrc == 0) x[r] = ldg<float>(sp[r], i);
-            else x[r] = widen1<kSrc>(ldg<uint16_t>(sp[r], i));
+            if constexpr (kMode == 0) x[r] = ldg<float>(ap[r], i);
+            else if constexpr (kMode == 1) x[r] = widen1<kGrad>(ldg<uint16_t>(gp[r], i));
+            else x[r] = ldg<float>(ap[r], i) + widen1<kGrad>(ldg<uint16_t>(gp[r], i));
         }
-        const float y = average(tree_sum<N>(x), inv_n, n_d);
+        const float y = average<N>(tree_sum<N>(x));
         stg<float>(out, i, y);
         ss += static_cast<double>(y) * static_cast<double>(y);
         bad += nonfinite(y);
@@ -295,19 +376,20 @@ __global__ void __launch_bounds__(kBlock) k_stats(const dp_chunk* __restrict__ c
 }
 
 // ============================================================================
-// pass 2: one workgroup folds the chunk partials in a fixed order and
-// updates the scalar state
+// pass 2: the chunk partials are folded in a fixed order -- by groups of
+// kFoldGroup when there are many -- and one workgroup updates the scalar state
 // ============================================================================
-__global__ void __launch_bounds__(kBlock) k_finalize(StatsBuf sb, int64_t nparts, DevState* __restrict__ st,
-                                                       ScalerArgs args) {
+template <typename Count>
+__device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, const Count* __restrict__ bad_in,
+                                           int64_t lo, int64_t hi, double& ss_out, uint64_t& bad_out) {
     __shared__ double s_ss[kBlock];
     __shared__ uint64_t s_bad[kBlock];
     const int tid = threadIdx.x;
     double ss = 0.0;
     uint64_t bad = 0;
-    for (int64_t i = tid; i < nparts; i += kBlock) {
-        ss += sb.sumsq[i];
-        bad += sb.bad[i];
+    for (int64_t i = lo + tid; i < hi; i += kBlock) {
+        ss += ss_in[i];
+        bad += bad_in[i];
     }
     s_ss[tid] = ss;
     s_bad[tid] = bad;
@@ -319,11 +401,32 @@ __global__ void __launch_bounds__(kBlock) k_finalize(StatsBuf sb, int64_t nparts
         }
         __syncthreads();
     }
-    if (tid != 0) return;
+    ss_out = s_ss[0];
+    bad_out = s_bad[0];
+}
+
+__global__ void __launch_bounds__(kBlock) k_fold(StatsBuf sb, int64_t nparts, FoldBuf fold) {
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFoldGroup;
+    const int64_t hi = lo + kFoldGroup < nparts ? lo + kFoldGroup : nparts;
+    double ss;
+    uint64_t bad;
+    block_fold(sb.sumsq, sb.bad, lo, hi, ss, bad);
+    if (threadIdx.x == 0) {
+        fold.sumsq[blockIdx.x] = ss;
+        fold.bad[blockIdx.x] = bad;
+    }
+}
+
+template <typename Count>
+__global__ void __launch_bounds__(kBlock) k_finalize(const double* __restrict__ ss_in, const Count* __restrict__ bad_in,
+                                                       int64_t nparts, DevState* __restrict__ st, ScalerArgs args) {
+    double sumsq;
+    uint64_t badsum;
+    block_fold(ss_in, bad_in, 0, nparts, sumsq, badsum);
+    if (threadIdx.x != 0) return;
     DevState s = *st;
-    const double sumsq = s_ss[0];
     s.sumsq = sumsq;
-    s.found_inf = s_bad[0] != 0 ? 1 : 0;
+    s.found_inf = badsum != 0 ? 1 : 0;
     s.norm = sqrt(sumsq) / s.scale;
     if (s.found_inf) {
         s.clip = 1.0;
@@ -373,14 +476,19 @@ __global__ void k_state_init(DevState* __restrict__ st, double scale) {
 // element; binary64 arithmetic, binary32 storage
 // ============================================================================
 struct AdamCoef {
-    double gscale, b1, omb1, b2, omb2, step, isb2, eps, dec;
+    double gscale, b1, omb1, b2, omb2, step, sqrt_bc2, eps, dec;
 };
 
+// One element of the update.  Every operation is a separately rounded IEEE
+// binary64 operation in the order written (no contraction into fused
+// multiply-adds), so the result depends on the inputs only, not on the
+// instruction selection.
 __device__ __forceinline__ void adam1(float gb, float& w, float& m, float& v, const AdamCoef& k) {
+#pragma clang fp contract(off)
     const double g = static_cast<double>(gb) * k.gscale;
     const double mi = k.b1 * static_cast<double>(m) + k.omb1 * g;
     const double vi = k.b2 * static_cast<double>(v) + k.omb2 * (g * g);
-    const double denom = sqrt(vi) * k.isb2 + k.eps;
+    const double denom = sqrt(vi) / k.sqrt_bc2 + k.eps;
     const double wi = static_cast<double>(w) * k.dec - k.step * (mi / denom);
     m = static_cast<float>(mi);
     v = static_cast<float>(vi);
@@ -393,15 +501,18 @@ __global__ void __launch_bounds__(kBlock) k_adamw(const dp_chunk* __restrict__ c
                                                     const DevState* __restrict__ st, AdamArgs args) {
     if (st->found_inf) return;
     AdamCoef k;
-    k.gscale = st->gscale;
-    k.b1 = args.beta1;
-    k.omb1 = 1.0 - args.beta1;
-    k.b2 = args.beta2;
-    k.omb2 = 1.0 - args.beta2;
-    k.step = args.lr / (1.0 - st->beta1_pow);
-    k.isb2 = 1.0 / sqrt(1.0 - st->beta2_pow);
-    k.eps = args.eps;
-    k.dec = 1.0 - args.lr * args.weight_decay;
+    {
+#pragma clang fp contract(off)
+        k.gscale = st->gscale;
+        k.b1 = args.beta1;
+        k.omb1 = 1.0 - args.beta1;
+        k.b2 = args.beta2;
+        k.omb2 = 1.0 - args.beta2;
+        k.step = args.lr / (1.0 - st->beta1_pow);
+        k.sqrt_bc2 = sqrt(1.0 - st->beta2_pow);
+        k.eps = args.eps;
+        k.dec = 1.0 - args.lr * args.weight_decay;
+    }
 
     const int64_t cid = base + blockIdx.x;
     const dp_chunk c = chunks[cid];
@@ -469,20 +580,20 @@ hipError_t for_pieces(int64_t nchunks, F&& launch) {
     return hipSuccess;
 }
 
-template <int kSrc, int N>
-hipError_t reduce_n(const dp_chunk* chunks, int64_t nchunks, const Srcs& srcs, RoleRef gbar, float inv_n, double n_d,
+template <int kMode, int kGrad, int N>
+hipError_t reduce_n(const dp_chunk* chunks, int64_t nchunks, const Srcs& accs, const Srcs& grads, RoleRef gbar,
                     StatsBuf sb, hipStream_t s) {
     return for_pieces(nchunks, [&](int64_t b, dim3 grid) {
-        hipLaunchKernelGGL((k_reduce<kSrc, N>), grid, dim3(kBlock), 0, s, chunks, b, srcs, gbar, inv_n, n_d, sb);
+        hipLaunchKernelGGL((k_reduce<kMode, kGrad, N>), grid, dim3(kBlock), 0, s, chunks, b, accs, grads, gbar, sb);
     });
 }
 
-template <int kSrc>
-hipError_t reduce_dispatch(int n, const dp_chunk* chunks, int64_t nchunks, const Srcs& srcs, RoleRef gbar,
-                           float inv_n, double n_d, StatsBuf sb, hipStream_t s) {
+template <int kMode, int kGrad>
+hipError_t reduce_dispatch(int n, const dp_chunk* chunks, int64_t nchunks, const Srcs& accs, const Srcs& grads,
+                           RoleRef gbar, StatsBuf sb, hipStream_t s) {
     switch (n) {
 #define DP_CASE(K) \
-    case K: return reduce_n<kSrc, K>(chunks, nchunks, srcs, gbar, inv_n, n_d, sb, s);
+    case K: return reduce_n<kMode, kGrad, K>(chunks, nchunks, accs, grads, gbar, sb, s);
         DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
         DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
 #undef DP_CASE
@@ -508,14 +619,29 @@ hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const dp_chun
     });
 }
 
-hipError_t launch_reduce(dp_dtype src_dt, int n, const dp_chunk* chunks, int64_t nchunks, const Srcs& srcs,
-                         RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    const bool pow2 = n > 0 && (n & (n - 1)) == 0;
-    const float inv_n = pow2 ? 1.0f / static_cast<float>(n) : 0.0f;
-    const double n_d = static_cast<double>(n);
-    if (src_dt == DP_F32) return reduce_dispatch<0>(n, chunks, nchunks, srcs, gbar, inv_n, n_d, sb, s);
-    if (src_dt == DP_F16) return reduce_dispatch<1>(n, chunks, nchunks, srcs, gbar, inv_n, n_d, sb, s);
-    return reduce_dispatch<2>(n, chunks, nchunks, srcs, gbar, inv_n, n_d, sb, s);
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const dp_chunk* chunks, int64_t nchunks,
+                                 const Srcs& grads, const Srcs& accs, hipStream_t s) {
+    return for_pieces(nchunks * n, [&](int64_t b, dim3 grid) {
+        const dim3 blk(kBlock);
+        if (gdt == DP_BF16) {
+            if (first) hipLaunchKernelGGL((k_accumulate_all<2, true>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+            else hipLaunchKernelGGL((k_accumulate_all<2, false>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+        } else {
+            if (first) hipLaunchKernelGGL((k_accumulate_all<1, true>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+            else hipLaunchKernelGGL((k_accumulate_all<1, false>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+        }
+    });
+}
+
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const dp_chunk* chunks, int64_t nchunks,
+                         const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<0, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+    if (mode == ReduceMode::kGradients) {
+        if (gdt == DP_F16) return reduce_dispatch<1, 1>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+        return reduce_dispatch<1, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+    }
+    if (gdt == DP_F16) return reduce_dispatch<2, 1>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+    return reduce_dispatch<2, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
 }
 
 hipError_t launch_stats(const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, StatsBuf sb, hipStream_t s) {
@@ -524,8 +650,17 @@ hipError_t launch_stats(const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, S
     });
 }
 
-hipError_t launch_finalize(StatsBuf sb, int64_t nparts, DevState* st, const ScalerArgs& args, hipStream_t s) {
-    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kBlock), 0, s, sb, nparts, st, args);
+hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
+                           hipStream_t s) {
+    if (nparts <= kFoldGroup) {
+        hipLaunchKernelGGL(k_finalize<uint32_t>, dim3(1), dim3(kBlock), 0, s, sb.sumsq, sb.bad, nparts, st, args);
+        return hipGetLastError();
+    }
+    const int64_t groups = (nparts + kFoldGroup - 1) / kFoldGroup;
+    hipLaunchKernelGGL(k_fold, dim3(static_cast<unsigned>(groups)), dim3(kBlock), 0, s, sb, nparts, fold);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_finalize<uint64_t>, dim3(1), dim3(kBlock), 0, s, fold.sumsq, fold.bad, groups, st, args);
     return hipGetLastError();
 }
 

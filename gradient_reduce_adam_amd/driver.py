@@ -1,10 +1,20 @@
 """A whole data-parallel step on one GPU through the C ABI.
 
 ``DPStep`` allocates the state in HBM with torch (memory only), binds it to a
-plan and issues, per step: n*a ``dp_accumulate`` calls (or, for incoming
-low-precision partials, none), one ``dp_reduce_replicas``, one
-``dp_grad_stats`` and one ``dp_adam_step`` per shard range.  Gradients come
-from a caller-supplied producer, standing in for the backward pass.
+plan and issues one step as:
+
+* fused (default): ``dp_accumulate_all`` for micro-steps 1 .. a-1 (every
+  replica in one launch), then ``dp_accumulate_reduce`` for micro-step a (the
+  last accumulation fused with the replica average); with a = 1 or incoming
+  partials only the latter;
+* per replica: ``dp_accumulate`` for every (micro-step, replica), then
+  ``dp_reduce_replicas`` (with n = 1 the last accumulation writes the
+  statistics instead);
+
+then ``dp_grad_stats`` and one ``dp_adam_step`` per shard range.  Both
+sequences give the same bits.  Gradients come from a caller-supplied
+producer, standing in for the backward pass; the fused sequence needs the n
+replicas' gradients of one micro-step at once.
 
 HBM layout (flat parameter space of P elements, tensors in list order):
 master, exp_avg, exp_avg_sq: binary32 [P]; param: bf16/fp16 [P];
@@ -37,10 +47,10 @@ class DPStep:
                  beta2: float = 0.999, max_norm: float = 0.0, scaler: str = "none", init_scale: float = 1.0,
                  backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, partials: bool = False,
                  shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
-                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None):
+                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True):
         if partials and a != 1:
             raise ValueError("incoming partials are reduced directly: a must be 1")
-        self.n, self.a, self.partials = n, a, partials
+        self.n, self.a, self.partials, self.fused = n, a, partials, fused
         self.lr, self.eps, self.weight_decay, self.max_norm = lr, eps, weight_decay, max_norm
         self.scaler = scaler
         self.plan = Plan(numel, n, grad_dtype, param_dtype, chunk_elems)
@@ -81,15 +91,20 @@ class DPStep:
     # -- one step ---------------------------------------------------------
     def issue_gradients(self, produce: GradProducer, step: int) -> None:
         """The accumulation (or partial) part of a step, up to g_bar."""
-        pl, st = self.plan, self.stream.cuda_stream
-        if self.partials:
+        pl, st, h = self.plan, self.stream.cuda_stream, self.plan.handle
+        if self.partials or self.fused:
+            last = 1 if self.partials else self.a
+            for k in range(1, last):
+                for r in range(self.n):
+                    dp_plan_bind_flat(h, DP_ROLE_GRAD, r, produce(step, r, k, self.scale))
+                pl.accumulate_all(first=(k == 1), stream=st)
             for r in range(self.n):
-                dp_plan_bind_flat(pl.handle, DP_ROLE_GRAD, r, produce(step, r, 1, self.scale))
-            pl.reduce_replicas("grad", stream=st)
+                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, produce(step, r, last, self.scale))
+            pl.accumulate_reduce(stream=st)
             return
         for k in range(1, self.a + 1):
             for r in range(self.n):
-                dp_plan_bind_flat(pl.handle, DP_ROLE_GRAD, r, produce(step, r, k, self.scale))
+                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, produce(step, r, k, self.scale))
                 pl.accumulate(r, first=(k == 1), emit_stats=(self.n == 1 and k == self.a), stream=st)
         if self.n > 1:
             pl.reduce_replicas("acc", stream=st)

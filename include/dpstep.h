@@ -48,7 +48,7 @@ extern "C" {
 
 #define DP_ABI_VERSION 1
 #define DP_MAX_REPLICAS 16
-#define DP_DEFAULT_CHUNK 65536
+#define DP_DEFAULT_CHUNK 2048
 
 typedef enum dp_status {
     DP_OK = 0,
@@ -135,6 +135,7 @@ typedef struct dp_plan_info {
     double bytes_accumulate;        /* read g and g_r, write g_r */
     double bytes_reduce_acc;        /* read n accumulators, write g_bar */
     double bytes_reduce_partials;   /* read n low-precision partials, write g_bar */
+    double bytes_accumulate_reduce; /* read n accumulators and n gradients, write g_bar */
     double bytes_stats_scan;        /* read g_bar */
     double bytes_adam;              /* read g_bar, w, m, v; write w, m, v, p */
 } dp_plan_info;
@@ -199,6 +200,24 @@ dp_status dp_state_init(dp_plan* plan, const dp_state_cfg* cfg, hipStream_t stre
  * micro-step replaces the scan of dp_grad_stats.  DP_ERR_STATE: first == 0 on
  * a replica with no first micro-step since the last reduction. */
 dp_status dp_accumulate(dp_plan* plan, int32_t replica, int32_t first, int32_t emit_stats, hipStream_t stream);
+
+/* Every replica's micro-step at once: the same as dp_accumulate(r, first, 0)
+ * for r = 0 .. n-1 in one launch.  The pages have every micro-step run on all
+ * n devices at the same time [first page, averaging formula paragraph]; here
+ * the n replicas' gradients are n buffers (GRAD[r]) of one GPU.  DP_ERR_STATE
+ * if the replicas are at different micro-steps, or first == 0 before a first
+ * micro-step. */
+dp_status dp_accumulate_all(dp_plan* plan, int32_t first, hipStream_t stream);
+
+/* The last micro-step fused with the replica average: GBAR = (sum_r
+ * (ACC[r] + GRAD[r])) / n in the order of dp_reduce_replicas, plus the
+ * per-chunk statistics; bit for bit the result of dp_accumulate on every
+ * replica followed by dp_reduce_replicas(DP_ROLE_ACC), but ACC[r] is read and
+ * not written back (it keeps the sum of the earlier micro-steps).  With no
+ * earlier micro-step since the last reduction (a = 1, or incoming partials)
+ * it is GBAR = (sum_r GRAD[r]) / n.  DP_ERR_STATE if the replicas are at
+ * different micro-steps or before dp_state_init. */
+dp_status dp_accumulate_reduce(dp_plan* plan, hipStream_t stream);
 
 /* Replica average [first page, averaging formula and reduction-order
  * paragraph]: GBAR = (sum_r SRC[r]) / n over [0, P) with a fixed pairwise order

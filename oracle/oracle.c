@@ -36,6 +36,12 @@ enum { OR_SCALER_NONE = 0, OR_SCALER_STATIC = 1, OR_SCALER_DYNAMIC = 2 };
 /* formats: binary16 and bfloat16, from their definitions                    */
 /* ------------------------------------------------------------------------ */
 
+/* 2^k for k = -25 .. 6 (hexadecimal literals: exact). */
+static const double pow2_table[32] = {
+    0x1p-25, 0x1p-24, 0x1p-23, 0x1p-22, 0x1p-21, 0x1p-20, 0x1p-19, 0x1p-18, 0x1p-17, 0x1p-16, 0x1p-15, 0x1p-14, 0x1p-13, 0x1p-12, 0x1p-11, 0x1p-10, 0x1p-9, 0x1p-8, 0x1p-7, 0x1p-6, 0x1p-5, 0x1p-4, 0x1p-3, 0x1p-2, 0x1p-1, 0x1p0, 0x1p1, 0x1p2, 0x1p3, 0x1p4, 0x1p5, 0x1p6};
+
+static double pow2(int k) { return pow2_table[k + 25]; }
+
 /* Value of a binary16 bit pattern: 1 sign, 5 exponent (bias 15), 10 fraction. */
 static double f16_value(uint16_t h) {
     int sign = (h >> 15) & 1;
@@ -43,9 +49,9 @@ static double f16_value(uint16_t h) {
     int f = h & 0x3FF;
     double mag;
     if (e == 0x1F) mag = f ? NAN : INFINITY;
-    else if (e == 0) mag = ldexp((double)f, -24);            /* subnormal: f * 2^-24 */
-    else mag = ldexp((double)(1024 + f), e - 25);            /* (1 + f/1024) * 2^(e-15) */
-    return sign ? -mag : mag;
+    else if (e == 0) mag = (double)f * pow2(-24);            /* subnormal: f * 2^-24 */
+    else mag = (double)(1024 + f) * pow2(e - 25);            /* (1 + f/1024) * 2^(e-15) */
+    return (1.0 - 2.0 * sign) * mag;                          /* times +1 or -1: exact */
 }
 
 /* Value of a bfloat16 bit pattern: the upper half of a binary32. */

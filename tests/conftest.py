@@ -10,7 +10,7 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: full-size workload, minutes of host work")
+    config.addinivalue_line("markers", "slow: a workload at full size (tens of seconds of oracle time)")
 
 
 def _ensure_built():

@@ -17,7 +17,7 @@ import oracle
 import synth
 from gradient_reduce_adam_amd import driver
 
-THREADS = int(os.environ.get("DP_ORACLE_THREADS", str(min(16, os.cpu_count() or 8))))
+THREADS = int(os.environ.get("DP_ORACLE_THREADS", str(min(16, len(os.sched_getaffinity(0))))))
 
 # Tolerances stated for the step: binary32 master, m, v within 2e-6 relative
 # with a 1e-9 absolute floor; the gradient norm within 1e-5 relative;
@@ -38,14 +38,14 @@ def log(msg: str) -> None:
 class GpuRun:
     """A workload on the GPU: the library's driver plus device-generated inputs."""
 
-    def __init__(self, w, shards=None, chunk_elems: int = 0, grad_slots: Optional[int] = None):
+    def __init__(self, w, shards=None, chunk_elems: int = 0, fused: bool = True):
         self.w = w
         self.d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                                weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                                scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                                growth_interval=w.growth_interval, partials=w.partials, shards=shards,
-                               chunk_elems=chunk_elems)
-        slots = w.n if w.partials else 1
+                               chunk_elems=chunk_elems, fused=fused)
+        slots = w.n if (w.partials or fused) else 1  # the fused step holds every replica's gradient at once
         self.slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(slots)]
         self.stream = self.d.stream.cuda_stream
         self.d.set_master(lambda ptr: synth.master_device(w, ptr, self.stream))

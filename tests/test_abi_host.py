@@ -22,7 +22,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     assert sorted(dp.EXPORTS) == names
     for n in names:
         assert hasattr(dp.lib, n), n
@@ -77,13 +77,16 @@ def test_chunk_table_matches_brute_force(numel, chunk):
 
 
 def test_chunk_table_of_a_2pow32_tensor_uses_64bit_indices():
-    with dp.Plan((1 << 32, 7), 4, "f16", "f16") as p:
+    with dp.Plan((1 << 32, 7), 4, "f16", "f16", 65536) as p:
         c = p.chunks()
         assert len(c) == (1 << 32) // 65536 + 1
         assert int(c[-2]["flat"]) == (1 << 32) - 65536 and int(c[-1]["flat"]) == 1 << 32
         assert int(c[-1]["offset"]) == 0 and int(c[-1]["tensor"]) == 1 and int(c[-1]["len"]) == 7
         mid = p.chunks((1 << 31) + 5, (1 << 31) + 70000)
         assert int(mid[0]["offset"]) == (1 << 31) + 5 and int(mid[0]["len"]) == 65531
+    with dp.Plan((1 << 32,), 1, "bf16", "bf16") as p:
+        assert p.info()["chunk_elems"] == dp.DP_DEFAULT_CHUNK == 2048
+        assert p.info()["num_chunks"] == (1 << 32) // 2048
 
 
 def test_plan_info_byte_model():
@@ -96,6 +99,7 @@ def test_plan_info_byte_model():
         assert info["bytes_accumulate_first"] == 6 * P and info["bytes_accumulate"] == 10 * P
         assert info["bytes_reduce_acc"] == (4 * 8 + 4) * P and info["bytes_reduce_partials"] == (2 * 8 + 4) * P
         assert info["bytes_adam"] == 30 * P and info["bytes_stats_scan"] == 4 * P
+        assert info["bytes_accumulate_reduce"] == ((2 + 4) * 8 + 4) * P
         assert info["num_chunks"] == len(p.chunks())
 
 
@@ -127,6 +131,12 @@ def test_bind_and_call_errors_before_any_launch():
         assert e.value.status == dp.DP_ERR_INVALID_ARG
         with pytest.raises(dp.DpError) as e:
             dp.dp_grad_stats(h, False, 1.0, stream=0)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate_all(h, True, stream=0)  # GRAD of replica 1 unbound
+        assert e.value.status == dp.DP_ERR_UNBOUND
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate_reduce(h, stream=0)  # before dp_state_init
         assert e.value.status == dp.DP_ERR_STATE
         with pytest.raises(dp.DpError) as e:
             dp.dp_reduce_replicas(h, dp.DP_ROLE_ACC, stream=0)

@@ -1,0 +1,72 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (default chunk size, the fused step sequence).
+
+The oracle computes the global statistics of every step over the whole flat
+range (they decide clipping and skipping) and the update on sampled windows:
+the first and last elements, windows straddling tensor and chunk boundaries,
+windows around every injected non-finite value, and seeded random windows.
+Two properties are checked at full size as well: the sum of squares the
+library reports is the binary64 sum of squares of its own g_bar (a torch
+reduction), and the skip flag is set exactly when that g_bar holds an inf or
+NaN."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads
+
+from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run, sample_windows
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+# steps per workload: every step of the workload where the oracle's full
+# statistics pass stays within tens of seconds of host time
+CASES = [("gpt2_small", 4), ("zero3_rank_7b", 5), ("unsharded_7b", 2), ("tp_column_slice", 1)]
+
+
+def _sumsq_fp64(x: torch.Tensor) -> float:
+    piece = 1 << 27
+    tot = torch.zeros((), dtype=torch.float64, device=x.device)
+    for i in range(0, x.numel(), piece):
+        tot += x[i:i + piece].double().square().sum()
+    return float(tot.item())
+
+
+def _nonfinite(x: torch.Tensor) -> bool:
+    piece = 1 << 27
+    return any(bool((~torch.isfinite(x[i:i + piece])).any()) for i in range(0, x.numel(), piece))
+
+
+@pytest.mark.parametrize("name,steps", CASES)
+def test_full_size_sampled_parity(name, steps):
+    w = workloads.by_name(name)
+    wins = sample_windows(w)
+    log(f"full size {name}: P={w.P} T={w.T} n={w.n} a={w.a} steps={steps} windows={len(wins)} "
+        f"({sum(h - l for l, h in wins)} elements)")
+    t0 = time.time()
+    run = GpuRun(w)
+    try:
+        states = run.run(steps)
+        got = {win: run.window(*win) for win in wins}
+        ss = _sumsq_fp64(run.d.gbar)
+        bad = _nonfinite(run.d.gbar)
+    finally:
+        run.close()
+    log(f"  gpu done in {time.time() - t0:.1f} s; last norm {states[-1]['norm']:.6g} clip {states[-1]['clip']:.6g}")
+    assert abs(states[-1]["sumsq"] - ss) <= 1e-12 * ss, (states[-1]["sumsq"], ss)
+    assert states[-1]["found_inf"] == int(bad)
+
+    t0 = time.time()
+    ref = oracle_run(w, steps, windows=wins, keep_gbar=(steps,))
+    log(f"  oracle done in {time.time() - t0:.1f} s")
+    for s, (g, r) in enumerate(zip(states, ref.scalars), start=1):
+        assert_scalars_match(g, r, where=f"{name} step {s}")
+    worst = {}
+    for win in wins:
+        rep = assert_state_close(got[win], ref.state[win], where=f"{name} window {win}")
+        for k, v in rep.items():
+            worst[k] = max(worst.get(k, 0), v)
+        assert np.array_equal(got[win]["gbar"].view(np.uint32), ref.gbar[steps][win].view(np.uint32)), win
+    log(f"  max ulp over windows: {worst}")

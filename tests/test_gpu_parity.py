@@ -43,7 +43,9 @@ def test_accumulators_and_gbar_bit_exact(gdt, n, a, chunk):
     w = workloads.gpt2_small().with_(numel=(3000, 17, 4096, 5, 70001, 256, 1, 65536), n=n, a=a, grad_dtype=gdt,
                                      param_dtype=gdt, scaled_tensors=(2,), steps=1)
     log(f"accumulate/reduce {gdt} n={n} a={a} chunk={chunk} P={w.P}")
-    run = GpuRun(w, chunk_elems=chunk)
+    ref_gbar = oracle_run(w, 1, keep_gbar=(1,)).gbar[1][(0, w.P)]
+    # per-replica calls: every accumulator, then g_bar
+    run = GpuRun(w, chunk_elems=chunk, fused=False)
     try:
         run.d.issue_gradients(run.produce, 1)
         torch.cuda.synchronize()
@@ -53,7 +55,23 @@ def test_accumulators_and_gbar_bit_exact(gdt, n, a, chunk):
                 oracle.accumulate(ref, synth.grad_host(w, 1, r, k, 0, w.P, 1.0), gdt, first=(k == 1))
             got = run.d.acc[r].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"acc[{r}]"
-        ref_gbar = oracle_run(w, 1, keep_gbar=(1,)).gbar[1][(0, w.P)]
+        assert np.array_equal(run.d.gbar.cpu().numpy().view(np.uint32), ref_gbar.view(np.uint32))
+    finally:
+        run.close()
+    # all replicas per launch, the last micro-step fused with the reduction:
+    # the accumulators hold micro-steps 1 .. a-1, g_bar the same bits
+    run = GpuRun(w, chunk_elems=chunk, fused=True)
+    try:
+        run.d.issue_gradients(run.produce, 1)
+        torch.cuda.synchronize()
+        if n > 1:
+            for r in range(n):
+                ref = np.empty(w.P, np.float32)
+                for k in range(1, a):
+                    oracle.accumulate(ref, synth.grad_host(w, 1, r, k, 0, w.P, 1.0), gdt, first=(k == 1))
+                if a > 1:
+                    got = run.d.acc[r].cpu().numpy()
+                    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"fused acc[{r}]"
         assert np.array_equal(run.d.gbar.cpu().numpy().view(np.uint32), ref_gbar.view(np.uint32))
     finally:
         run.close()
@@ -118,6 +136,9 @@ VARIANTS = {
     "n16": dict(base="tiny", numel=(65536 * 3 + 11,), n=16, a=1, steps=3),
     "f16_partials_n2": dict(base="zero3_rank_7b", numel=(100000, 3), n=2, a=1, grad_dtype="f16",
                             param_dtype="f16", init_scale=1024.0, injections=(), steps=3),
+    # more chunks than one fold group: the statistics fold in two levels
+    "two_level_fold": dict(base="gpt2_small", numel=(3000011, 1999999, 5), n=2, a=2, max_norm=0.5,
+                           scaled_tensors=(1,), chunk=256, steps=3),
     # parameter dtype different from the gradient dtype
     "bf16_grad_f16_param": dict(base="tiny", numel=RAGGED, n=2, a=2, grad_dtype="bf16", param_dtype="f16",
                                 steps=3),
@@ -132,6 +153,32 @@ def test_variant_full_parity(name):
     steps = spec.pop("steps")
     w = base.with_(**spec)
     _full_parity(w, steps, chunk=chunk, label=name)
+
+
+@pytest.mark.parametrize("name", ["bf16_clip_n3", "f16_static_n5", "n1_fused_stats", "dynamic_partials"])
+def test_per_replica_sequence_equals_fused_bitwise(name):
+    """dp_accumulate per (micro-step, replica) + dp_reduce_replicas and
+    dp_accumulate_all + dp_accumulate_reduce give the same bits."""
+    spec = dict(VARIANTS[name])
+    base = workloads.by_name(spec.pop("base"))
+    chunk = spec.pop("chunk", 0)
+    steps = min(spec.pop("steps"), 4)
+    w = base.with_(**spec)
+    log(f"per-replica vs fused {name}")
+    outs = []
+    for fused in (False, True):
+        run = GpuRun(w, chunk_elems=chunk, fused=fused)
+        try:
+            st = run.run(steps)
+            outs.append((run.window(0, w.P), st))
+        finally:
+            run.close()
+    (a, sa), (b, sb) = outs
+    for k in ("w", "m", "v", "p", "gbar"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    for x, y in zip(sa, sb):  # same bits, NaN statistics of skipped steps included
+        assert np.array_equal(np.array(list(x.values()), np.float64).view(np.uint64),
+                              np.array(list(y.values()), np.float64).view(np.uint64))
 
 
 def test_sharded_update_equals_unsharded_bitwise():
