@@ -41,7 +41,64 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1 << 22, help="params in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/traffic.json, then exit")
     return ap.parse_args()
+
+
+# rocprofv3 kernel names of each call kind (substring of the demangled name)
+KERNEL_NAMES = {
+    "accumulate_first": "k_accumulate_all<2, true>",
+    "accumulate": "k_accumulate_all<2, false>",
+    "accumulate_reduce": "k_reduce<",
+    "adamw": "k_adamw<",
+}
+COPY_KERNEL = "copyBuffer"  # the runtime's plain device-to-device copy
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calib_bytes: int) -> dict:
+    """Per-launch HBM bytes of each kernel kind from the FETCH_SIZE and
+    WRITE_SIZE counters (KiB per dispatch), each scaled by the factor that
+    maps the same counter on a plain copy of calib_bytes to the bytes that
+    copy must move (calib_bytes read, calib_bytes written)."""
+    import csv
+
+    def load(path, counter):
+        rows = {}
+        for r in csv.DictReader(open(path)):
+            if r.get("Counter_Name", counter) != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            rows.setdefault(name, []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch = load(fetch_csv, "FETCH_SIZE")
+    write = load(write_csv, "WRITE_SIZE")
+
+    def per_kind(rows, key):
+        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    copy_f = [v for name, vs in fetch.items() if COPY_KERNEL in name and "dpk" not in name for v in vs]
+    copy_w = [v for name, vs in write.items() if COPY_KERNEL in name and "dpk" not in name for v in vs]
+    # the copies of calib_bytes are the largest copy dispatches
+    f_kib = sorted(copy_f)[-1]
+    w_kib = sorted(copy_w)[-1]
+    f_fac = calib_bytes / (f_kib * 1024.0)
+    w_fac = calib_bytes / (w_kib * 1024.0)
+    out = {}
+    for kind, key in KERNEL_NAMES.items():
+        fk, wk = per_kind(fetch, key), per_kind(write, key)
+        if fk is None or wk is None:
+            continue
+        out[kind] = {"fetch_kib": fk, "write_kib": wk, "copy_factor_fetch": f_fac, "copy_factor_write": w_fac,
+                     "bytes_per_launch": fk * 1024.0 * f_fac + wk * 1024.0 * w_fac,
+                     "kernel_source_sha": kernel_source_hash()}
+    return {workload: out, "calibration": {"copy_bytes": calib_bytes, "fetch_kib": f_kib, "write_kib": w_kib}}
 
 
 def kernel_source_hash() -> str:
@@ -72,13 +129,20 @@ def launch_bytes(w, kind: str) -> float:
     return w.P * per[kind] / launches.get(kind, 1)
 
 
-def run_gpu(w, steps: int, warmup: int, chunk: int = 0):
+def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0):
     import torch
 
     import synth
     from gradient_reduce_adam_amd import DP_ROLE_GRAD, dp_plan_bind_flat, driver
 
     torch.cuda.set_device(0)
+    if calib:
+        src = torch.empty(calib, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
@@ -185,8 +249,19 @@ def main():
         sys.exit(2)
     from synth import workloads
 
+    if args.summarize_counters:
+        res = summarize_counters(*args.summarize_counters, args.workload, args.copy_calibration)
+        old = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                old = json.load(f)
+        old.update(res)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(old, f, indent=1)
+        print(json.dumps(res, indent=1))
+        return
     w = workloads.by_name(args.workload)
-    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk)
+    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w)
     step_bytes = sum(per_param.values()) * w.P
