@@ -28,7 +28,7 @@ DP_F32, DP_F16, DP_BF16 = 0, 1, 2
  DP_ROLE_GBAR) = range(7)
 DP_SCALER_NONE, DP_SCALER_STATIC, DP_SCALER_DYNAMIC = 0, 1, 2
 DP_MAX_REPLICAS = 16
-DP_DEFAULT_CHUNK = 2048
+DP_DEFAULT_CHUNK = 16384
 
 DTYPES = {"f32": DP_F32, "f16": DP_F16, "bf16": DP_BF16}
 SCALERS = {"none": DP_SCALER_NONE, "static": DP_SCALER_STATIC, "dynamic": DP_SCALER_DYNAMIC}

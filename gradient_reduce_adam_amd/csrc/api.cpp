@@ -44,9 +44,19 @@ struct Binding {
 };
 
 struct DeviceTable {
-    int64_t begin = 0, end = 0, count = 0;
+    int64_t begin = 0, end = 0, count = 0;  // count: chunks
     dp_chunk* dev = nullptr;
+    int log2s = 0;
+
+    int64_t npieces() const { return count << log2s; }
+    dpk::Table table() const { return dpk::Table{dev, npieces(), log2s}; }
 };
+
+int log2_exact(int64_t x) {
+    int k = 0;
+    while ((int64_t{1} << k) < x) ++k;
+    return k;
+}
 
 size_t esize(dp_dtype d) { return d == DP_F32 ? 4 : 2; }
 
@@ -116,6 +126,7 @@ dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out)
     out->end = end;
     out->count = static_cast<int64_t>(host.size());
     out->dev = nullptr;
+    out->log2s = log2_exact(p->chunk / dpk::kPiece);
     if (host.empty()) return DP_OK;
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&out->dev), host.size() * sizeof(dp_chunk));
     if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of a %zu-entry chunk table: %s", host.size(), hipGetErrorString(e));
@@ -206,8 +217,8 @@ dp_status dp_plan_create(const dp_layout* L, dp_plan** out) {
     if (L->param_dtype != DP_F16 && L->param_dtype != DP_BF16)
         return fail(DP_ERR_BAD_LAYOUT, "param_dtype must be DP_F16 or DP_BF16");
     int32_t chunk = L->chunk_elems == 0 ? DP_DEFAULT_CHUNK : L->chunk_elems;
-    if (chunk < 256 || chunk > (1 << 26) || chunk % 256 != 0)
-        return fail(DP_ERR_BAD_LAYOUT, "chunk_elems %d must be a multiple of 256 in [256, 2^26]", L->chunk_elems);
+    if (chunk < dpk::kPiece || chunk > (1 << 26) || (chunk & (chunk - 1)) != 0)
+        return fail(DP_ERR_BAD_LAYOUT, "chunk_elems %d must be a power of two in [256, 2^26]", L->chunk_elems);
     dp_plan* p = new (std::nothrow) dp_plan();
     if (!p) return fail(DP_ERR_OOM, "dp_plan_create: host allocation failed");
     p->T = L->num_tensors;
@@ -365,7 +376,7 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     if (!p->state) {
         hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->state), sizeof(dpk::DevState));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of the state block: %s", hipGetErrorString(e));
-        const size_t np = static_cast<size_t>(std::max<int64_t>(p->full.count, 1));
+        const size_t np = static_cast<size_t>(std::max<int64_t>(p->full.npieces(), 1));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.sumsq), np * sizeof(double));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
@@ -408,8 +419,8 @@ dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit
     s = ensure_full(p);
     if (s != DP_OK) return s;
     if (p->full.count > 0) {
-        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, p->full.dev, p->full.count,
-                                                g.ref(), a.ref(), p->stats, stream),
+        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, p->full.table(), g.ref(), a.ref(),
+                                                p->stats, stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
@@ -436,8 +447,8 @@ static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs
     dp_status s = ensure_full(p);
     if (s != DP_OK) return s;
     if (p->full.count > 0) {
-        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, p->full.dev, p->full.count, accs, grads, gb->ref(),
-                                            p->stats, stream),
+        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, p->full.table(), accs, grads, gb->ref(), p->stats,
+                                            stream),
                          "reduce launch");
         if (s != DP_OK) return s;
     }
@@ -481,8 +492,7 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     s = ensure_full(p);
     if (s != DP_OK) return s;
     if (p->full.count > 0) {
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.dev, p->full.count, grads, accs,
-                                                    stream),
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.table(), grads, accs, stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
@@ -522,7 +532,7 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
         s = need(gb, "GBAR");
         if (s != DP_OK) return s;
         if (p->full.count > 0) {
-            s = check_launch(dpk::launch_stats(p->full.dev, p->full.count, gb->ref(), p->stats, stream), "stats launch");
+            s = check_launch(dpk::launch_stats(p->full.table(), gb->ref(), p->stats, stream), "stats launch");
             if (s != DP_OK) return s;
         }
     } else if (!p->partials_valid && p->full.count > 0) {
@@ -530,7 +540,7 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
     }
     dpk::ScalerArgs a{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, max_norm,
                       p->cfg.scaler_mode, p->cfg.growth_interval};
-    s = check_launch(dpk::launch_finalize(p->stats, p->full.count, p->fold, p->state, a, stream), "finalize launch");
+    s = check_launch(dpk::launch_finalize(p->stats, p->full.npieces(), p->fold, p->state, a, stream), "finalize launch");
     if (s != DP_OK) return s;
     p->partials_valid = false;
     p->stats_current = true;
@@ -558,7 +568,7 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
     s = range_table(p, begin, end, &t);
     if (s != DP_OK) return s;
     dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
-    return check_launch(dpk::launch_adamw(p->pdt, t->dev, t->count, gb->ref(), p->roles[DP_ROLE_MASTER][0].ref(),
+    return check_launch(dpk::launch_adamw(p->pdt, t->table(), gb->ref(), p->roles[DP_ROLE_MASTER][0].ref(),
                                           p->roles[DP_ROLE_EXP_AVG][0].ref(), p->roles[DP_ROLE_EXP_AVG_SQ][0].ref(),
                                           p->roles[DP_ROLE_PARAM][0].ref(), p->state, a, stream),
                         "adamw launch");

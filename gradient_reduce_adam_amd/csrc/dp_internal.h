@@ -9,8 +9,19 @@
 
 namespace dpk {
 
-constexpr int kBlock = 256;              // threads per workgroup: 4 wave64s
-constexpr int64_t kMaxBlocksPerLaunch = 1 << 20;
+constexpr int kWave = 64;                 // threads per streaming workgroup: one wave64
+constexpr int kPiece = 4 * kWave;         // elements per streaming workgroup: 4 per lane
+constexpr int kFoldThreads = 256;         // threads of the statistics fold workgroups
+constexpr int64_t kMaxBlocksPerLaunch = int64_t{1} << 24;  // keeps gridDim.x * kWave below 2^32
+
+// A chunk table on the device, as the kernels see it: npieces = chunks << log2s
+// single-wave pieces of kPiece elements (the last pieces of a short chunk are
+// empty).
+struct Table {
+    const dp_chunk* chunks;
+    int64_t npieces;
+    int log2s;  // log2(chunk_elems / kPiece)
+};
 
 // Where one role's memory is: a flat base (tensor i at element prefix[i]) or
 // a device table of per-tensor pointers.
@@ -33,15 +44,15 @@ struct DevState {
 };
 static_assert(sizeof(DevState) == sizeof(dp_step_state), "DevState must mirror dp_step_state");
 
-// Per-chunk statistics of g_bar: binary64 sum of squares and the count of
-// non-finite entries.  Index = position of the chunk in the [0, P) table.
+// Per-piece statistics of g_bar: binary64 sum of squares and the count of
+// non-finite entries.  Index = position of the piece in the [0, P) table.
 struct StatsBuf {
     double* sumsq;
     uint32_t* bad;
 };
 
 // Second level of the statistics fold: one entry per group of kFoldGroup
-// chunk partials (used when a table has more than kFoldGroup chunks).
+// piece partials (used when a table has more than kFoldGroup pieces).
 constexpr int64_t kFoldGroup = 4096;
 struct FoldBuf {
     double* sumsq;
@@ -57,10 +68,10 @@ struct ScalerArgs {
     int32_t mode, growth_interval;
 };
 
-hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const dp_chunk* chunks, int64_t nchunks,
-                             RoleRef grad, RoleRef acc, StatsBuf sb, hipStream_t stream);
-hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const dp_chunk* chunks, int64_t nchunks,
-                                 const Srcs& grads, const Srcs& accs, hipStream_t stream);
+hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
+                             StatsBuf sb, hipStream_t stream);
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
+                                 hipStream_t stream);
 
 // What each replica contributes to the reduction.
 enum class ReduceMode {
@@ -68,13 +79,13 @@ enum class ReduceMode {
     kGradients,     // g_r (the gradient dtype): partials, or a single micro-step
     kAccPlusGrad    // acc_r + g_r: the last micro-step fused, acc_r not written back
 };
-hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const dp_chunk* chunks, int64_t nchunks,
-                         const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t stream);
-hipError_t launch_stats(const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, StatsBuf sb, hipStream_t stream);
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
+                         RoleRef gbar, StatsBuf sb, hipStream_t stream);
+hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t stream);
-hipError_t launch_adamw(dp_dtype pdt, const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, RoleRef w, RoleRef m,
-                        RoleRef v, RoleRef p, const DevState* st, const AdamArgs& args, hipStream_t stream);
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
+                        const DevState* st, const AdamArgs& args, hipStream_t stream);
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t stream);
 
 }  // namespace dpk

@@ -1,13 +1,21 @@
 // gfx950 kernels of the data-parallel gradient reduce + AdamW step.
 //
-// Every streaming kernel walks a chunk table: workgroup b processes chunk
-// (base + b), a contiguous piece of one tensor of at most chunk_elems
-// elements.  A chunk whose pointers are all 16-byte aligned goes through
-// 16-byte vector loads and stores (wave64 reads 1 KiB contiguous per
-// instruction); any other chunk, and the ragged end of every chunk, takes a
-// scalar loop.  All reductions are fixed-order trees (wavefront butterflies,
-// then LDS across the four waves, then one partial per chunk), so results are
-// bitwise reproducible run to run; no floating-point atomics are used.
+// Work decomposition.  The plan's chunk table splits the flat parameter space
+// into chunks of at most chunk_elems elements, each inside one tensor (so a
+// chunk keeps its tensor's alignment).  Every streaming kernel runs one wave64
+// workgroup per 256-element piece of a chunk: piece p is piece (p & (S-1)) of
+// chunk (p >> log2 S), S = chunk_elems / 256.  A lane moves 4 consecutive
+// elements, so each binary32 stream is one 16-byte access per lane and one
+// contiguous KiB per wave, and a 16-bit stream one 8-byte access per lane.
+// Thousands of one-shot single-wave workgroups keep the addresses in flight
+// dense and spread over all HBM channels; measured on MI355X this beats
+// larger workgroups and persistent grid-stride loops by 10-25% on these
+// read-modify-write streams.  A piece whose pointers are not aligned, and the
+// ragged end of a chunk, take a per-element path.
+//
+// Reductions are fixed-order trees: a wave64 butterfly per piece writes one
+// binary64 partial, folded later in a fixed order, so results are bitwise
+// reproducible run to run.  No floating-point atomics are used.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -17,24 +25,14 @@
 namespace dpk {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-
-template <typename T>
-__device__ __forceinline__ T* elem_ptr(const RoleRef& r, const dp_chunk& c) {
-    if (r.tab) return static_cast<T*>(r.tab[c.tensor]) + c.offset;
-    return static_cast<T*>(r.base) + c.flat;
-}
-
-__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Memory access through the global address space (global_load / global_store
 // rather than flat_*: the pointers come from tables, so the compiler cannot
-// infer the address space itself).  _nt variants set the nontemporal hint
-// for data streamed once.
+// infer the address space itself).  _nt variants set the nontemporal hint for
+// data streamed once.
 #define DP_GLOBAL __attribute__((address_space(1)))
 
 template <typename V>
@@ -50,6 +48,32 @@ __device__ __forceinline__ void stg_nt(void* p, int64_t i, V x) {
     __builtin_nontemporal_store(x, ((DP_GLOBAL V*)p) + i);
 }
 
+__device__ __forceinline__ bool aligned(const void* p, uintptr_t bytes) {
+    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
+// ---- the piece a workgroup owns ----------------------------------------------
+struct Piece {
+    dp_chunk c;  // its chunk
+    int start;   // first element of the piece inside the chunk
+    int len;     // elements of the piece (0 .. kPiece)
+};
+
+__device__ __forceinline__ Piece piece_of(const dp_chunk* __restrict__ chunks, int64_t p, int log2s) {
+    Piece q;
+    q.c = chunks[p >> log2s];
+    q.start = static_cast<int>(p & ((int64_t{1} << log2s) - 1)) * kPiece;
+    const int rest = q.c.len - q.start;
+    q.len = rest < 0 ? 0 : (rest < kPiece ? rest : kPiece);
+    return q;
+}
+
+template <typename T>
+__device__ __forceinline__ T* elem_ptr(const RoleRef& r, const Piece& q) {
+    if (r.tab) return static_cast<T*>(r.tab[q.c.tensor]) + q.c.offset + q.start;
+    return static_cast<T*>(r.base) + q.c.flat + q.start;
+}
+
 // ---- low-precision formats --------------------------------------------------
 // kind: 1 = binary16, 2 = bfloat16 (dp_dtype values)
 template <int kind>
@@ -59,16 +83,12 @@ __device__ __forceinline__ float widen1(uint16_t b) {
 }
 
 template <int kind>
-__device__ __forceinline__ f32x8 widen8(u32x4 q) {
+__device__ __forceinline__ f32x4 widen4(u32x2 q) {
     if constexpr (kind == 2) {
-        f32x8 f;
-        f[0] = __uint_as_float(q.x << 16); f[1] = __uint_as_float(q.x & 0xFFFF0000u);
-        f[2] = __uint_as_float(q.y << 16); f[3] = __uint_as_float(q.y & 0xFFFF0000u);
-        f[4] = __uint_as_float(q.z << 16); f[5] = __uint_as_float(q.z & 0xFFFF0000u);
-        f[6] = __uint_as_float(q.w << 16); f[7] = __uint_as_float(q.w & 0xFFFF0000u);
-        return f;
+        return f32x4{__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
+                     __uint_as_float(q.y & 0xFFFF0000u)};
     } else {
-        return __builtin_convertvector(__builtin_bit_cast(f16x8, q), f32x8);
+        return __builtin_convertvector(__builtin_bit_cast(f16x4, q), f32x4);
     }
 }
 
@@ -83,24 +103,21 @@ __device__ __forceinline__ uint32_t nonfinite(float x) {
     return (__float_as_uint(x) & 0x7F800000u) == 0x7F800000u ? 1u : 0u;
 }
 
-// ---- deterministic block reduction of (sumsq, bad) -----------------------
-__device__ __forceinline__ void block_stats_store(double ss, uint32_t bad, int64_t cid, StatsBuf sb) {
-    __shared__ double s_ss[kBlock / 64];
-    __shared__ uint32_t s_bad[kBlock / 64];
+__device__ __forceinline__ void add_stats(float y, double& ss, uint32_t& bad) {
+    ss += static_cast<double>(y) * static_cast<double>(y);
+    bad += nonfinite(y);
+}
+
+// Fixed-order wave64 butterfly of (sumsq, bad); lane 0 writes partial p.
+__device__ __forceinline__ void wave_stats_store(double ss, uint32_t bad, int64_t p, StatsBuf sb) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         ss += __shfl_xor(ss, off, 64);
         bad += __shfl_xor(bad, off, 64);
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        s_ss[wave] = ss;
-        s_bad[wave] = bad;
-    }
-    __syncthreads();
     if (threadIdx.x == 0) {
-        sb.sumsq[cid] = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
-        sb.bad[cid] = s_bad[0] + s_bad[1] + s_bad[2] + s_bad[3];
+        sb.sumsq[p] = ss;
+        sb.bad[p] = bad;
     }
 }
 
@@ -138,263 +155,159 @@ __device__ __forceinline__ float average(float s) {
 // micro-step accumulation: acc = g (first) or acc + g
 // ============================================================================
 template <int kGrad, bool kFirst, bool kStats>
-__device__ __forceinline__ void accumulate_chunk(const dp_chunk& c, RoleRef grad, RoleRef acc, double& ss,
+__device__ __forceinline__ void accumulate_piece(const Piece& q, RoleRef grad, RoleRef acc, double& ss,
                                                  uint32_t& bad) {
-    const uint16_t* __restrict__ g = elem_ptr<const uint16_t>(grad, c);
-    float* __restrict__ a = elem_ptr<float>(acc, c);
-    const int len = c.len, tid = threadIdx.x;
-    const int nvec = (aligned16(g) && aligned16(a)) ? (len >> 3) : 0;  // 8 elements per vector
-    constexpr int U = 2;
-    for (int v0 = 0; v0 < nvec; v0 += kBlock * U) {
-        u32x4 gq[U];
-        f32x4 a0[U], a1[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kBlock + tid;
-            if (v < nvec) {
-                gq[u] = ldg_nt<u32x4>(g, v);
-                if constexpr (!kFirst) {
-                    a0[u] = ldg<f32x4>(a, 2 * v);
-                    a1[u] = ldg<f32x4>(a, 2 * v + 1);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kBlock + tid;
-            if (v < nvec) {
-                const f32x8 gf = widen8<kGrad>(gq[u]);
-                f32x4 r0 = {gf[0], gf[1], gf[2], gf[3]};
-                f32x4 r1 = {gf[4], gf[5], gf[6], gf[7]};
-                if constexpr (!kFirst) {
-                    r0 = a0[u] + r0;
-                    r1 = a1[u] + r1;
-                }
-                stg<f32x4>(a, 2 * v, r0);
-                stg<f32x4>(a, 2 * v + 1, r1);
-                if constexpr (kStats) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ss += static_cast<double>(r0[e]) * static_cast<double>(r0[e]);
-                        bad += nonfinite(r0[e]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ss += static_cast<double>(r1[e]) * static_cast<double>(r1[e]);
-                        bad += nonfinite(r1[e]);
-                    }
-                }
-            }
-        }
-    }
-    for (int i = nvec * 8 + tid; i < len; i += kBlock) {
-        const float gi = widen1<kGrad>(ldg<uint16_t>(g, i));
-        const float r = kFirst ? gi : ldg<float>(a, i) + gi;
-        stg<float>(a, i, r);
+    const uint16_t* __restrict__ g = elem_ptr<const uint16_t>(grad, q);
+    float* __restrict__ a = elem_ptr<float>(acc, q);
+    const int lane = threadIdx.x, e0 = lane * 4;
+    if (e0 + 4 <= q.len && aligned(g, 8) && aligned(a, 16)) {
+        f32x4 r = widen4<kGrad>(ldg_nt<u32x2>(g, lane));
+        if constexpr (!kFirst) r = ldg<f32x4>(a, lane) + r;
+        stg<f32x4>(a, lane, r);
         if constexpr (kStats) {
-            ss += static_cast<double>(r) * static_cast<double>(r);
-            bad += nonfinite(r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) add_stats(r[e], ss, bad);
+        }
+    } else {
+        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+            const float gi = widen1<kGrad>(ldg<uint16_t>(g, i));
+            const float r = kFirst ? gi : ldg<float>(a, i) + gi;
+            stg<float>(a, i, r);
+            if constexpr (kStats) add_stats(r, ss, bad);
         }
     }
 }
 
-// one replica; with kStats the chunk statistics of the result (n = 1: it is g_bar)
+// one replica; with kStats the piece statistics of the result (n = 1: it is g_bar)
 template <int kGrad, bool kFirst, bool kStats>
-__global__ void __launch_bounds__(kBlock) k_accumulate(const dp_chunk* __restrict__ chunks, int64_t base,
-                                                         RoleRef grad, RoleRef acc, StatsBuf sb) {
-    const int64_t cid = base + blockIdx.x;
-    const dp_chunk c = chunks[cid];
+__global__ void __launch_bounds__(kWave) k_accumulate(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
+                                                        RoleRef grad, RoleRef acc, StatsBuf sb) {
+    const int64_t p = base + blockIdx.x;
+    const Piece q = piece_of(chunks, p, log2s);
     double ss = 0.0;
     uint32_t bad = 0;
-    accumulate_chunk<kGrad, kFirst, kStats>(c, grad, acc, ss, bad);
-    if constexpr (kStats) block_stats_store(ss, bad, cid, sb);
+    accumulate_piece<kGrad, kFirst, kStats>(q, grad, acc, ss, bad);
+    if constexpr (kStats) wave_stats_store(ss, bad, p, sb);
 }
 
-// every replica's micro-step in one launch: workgroup b handles replica
-// b / nchunks, chunk b % nchunks (replica-major, so each replica's buffers are
-// streamed in order)
+// every replica's micro-step in one launch: blockIdx.y is the replica (the
+// dispatcher walks x fastest, so each replica's buffers stream in order)
 template <int kGrad, bool kFirst>
-__global__ void __launch_bounds__(kBlock) k_accumulate_all(const dp_chunk* __restrict__ chunks, int64_t nchunks,
-                                                             int64_t base, Srcs grads, Srcs accs) {
-    const int64_t b = base + blockIdx.x;
-    const int r = static_cast<int>(b / nchunks);
-    const dp_chunk c = chunks[b - static_cast<int64_t>(r) * nchunks];
+__global__ void __launch_bounds__(kWave) k_accumulate_all(const dp_chunk* __restrict__ chunks, int log2s,
+                                                            int64_t base, Srcs grads, Srcs accs) {
+    const Piece q = piece_of(chunks, base + blockIdx.x, log2s);
     double ss = 0.0;
     uint32_t bad = 0;
-    accumulate_chunk<kGrad, kFirst, false>(c, grads.r[r], accs.r[r], ss, bad);
+    accumulate_piece<kGrad, kFirst, false>(q, grads.r[blockIdx.y], accs.r[blockIdx.y], ss, bad);
 }
 
 // ============================================================================
-// replica reduction: gbar = tree(x_0..x_{N-1}) / N, plus chunk statistics
+// replica reduction: gbar = tree(x_0..x_{N-1}) / N, plus piece statistics
 //   kMode 0: x_r = acc_r                 (binary32 accumulators)
 //   kMode 1: x_r = g_r                   (low-precision gradients or partials)
 //   kMode 2: x_r = acc_r + g_r           (the last micro-step fused: acc_r is
 //                                         not written back)
-// Modes 0 and 2 move 4 elements per lane (one dwordx4 of each binary32
-// stream, a wave reads 1 KiB contiguous); mode 1 moves 8.
 // ============================================================================
-template <int N>
-__device__ __forceinline__ void reduce_store(float (&x)[4][N], float* out, int64_t q, double& ss, uint32_t& bad) {
-    float y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        y[e] = average<N>(tree_sum<N>(x[e]));
-        ss += static_cast<double>(y[e]) * static_cast<double>(y[e]);
-        bad += nonfinite(y[e]);
-    }
-    stg_nt<f32x4>(out, q, f32x4{y[0], y[1], y[2], y[3]});
-}
-
-template <int kind>
-__device__ __forceinline__ f32x4 widen4(u32x2 q) {
-    if constexpr (kind == 2) {
-        return f32x4{__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xFFFF0000u), __uint_as_float(q.y << 16),
-                     __uint_as_float(q.y & 0xFFFF0000u)};
-    } else {
-        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-        return __builtin_convertvector(__builtin_bit_cast(f16x4, q), f32x4);
-    }
-}
-
 template <int kMode, int kGrad, int N>
-__global__ void __launch_bounds__(kBlock) k_reduce(const dp_chunk* __restrict__ chunks, int64_t base, Srcs accs,
-                                                     Srcs grads, RoleRef gbar, StatsBuf sb) {
-    const int64_t cid = base + blockIdx.x;
-    const dp_chunk c = chunks[cid];
-    const int len = c.len, tid = threadIdx.x;
+__global__ void __launch_bounds__(kWave) k_reduce(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
+                                                    Srcs accs, Srcs grads, RoleRef gbar, StatsBuf sb) {
+    const int64_t p = base + blockIdx.x;
+    const Piece q = piece_of(chunks, p, log2s);
     const float* ap[N];
     const uint16_t* gp[N];
     bool ok = true;
 #pragma unroll
     for (int r = 0; r < N; ++r) {
         if constexpr (kMode != 1) {
-            ap[r] = elem_ptr<const float>(accs.r[r], c);
-            ok = ok && aligned16(ap[r]);
+            ap[r] = elem_ptr<const float>(accs.r[r], q);
+            ok = ok && aligned(ap[r], 16);
         }
         if constexpr (kMode != 0) {
-            gp[r] = elem_ptr<const uint16_t>(grads.r[r], c);
-            ok = ok && (reinterpret_cast<uintptr_t>(gp[r]) & (kMode == 1 ? 15u : 7u)) == 0;
+            gp[r] = elem_ptr<const uint16_t>(grads.r[r], q);
+            ok = ok && aligned(gp[r], 8);
         }
     }
-    float* __restrict__ out = elem_ptr<float>(gbar, c);
-    ok = ok && aligned16(out);
-    constexpr int kVec = kMode == 1 ? 8 : 4;  // elements per lane and iteration
-    constexpr int U = ((kMode == 0 && N <= 8) || (kMode == 2 && N <= 4)) ? 2 : 1;
-    const int nvec = ok ? len / kVec : 0;
+    float* __restrict__ out = elem_ptr<float>(gbar, q);
+    ok = ok && aligned(out, 16);
+    const int lane = threadIdx.x, e0 = lane * 4;
     double ss = 0.0;
     uint32_t bad = 0;
-    for (int v0 = 0; v0 < nvec; v0 += kBlock * U) {
-        if constexpr (kMode != 1) {
-            f32x4 q[U][N];
-            u32x2 h[U][N];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kBlock + tid;
-                if (v < nvec) {
-#pragma unroll
-                    for (int r = 0; r < N; ++r) {
-                        q[u][r] = ldg_nt<f32x4>(ap[r], v);
-                        if constexpr (kMode == 2) h[u][r] = ldg_nt<u32x2>(gp[r], v);
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kBlock + tid;
-                if (v < nvec) {
-                    float x[4][N];
-#pragma unroll
-                    for (int r = 0; r < N; ++r) {
-                        f32x4 t = q[u][r];
-                        if constexpr (kMode == 2) t = t + widen4<kGrad>(h[u][r]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e][r] = t[e];
-                    }
-                    reduce_store<N>(x, out, v, ss, bad);
-                }
-            }
-        } else {
-            const int v = v0 + tid;
-            if (v < nvec) {
-                f32x8 f[N];
-#pragma unroll
-                for (int r = 0; r < N; ++r) f[r] = widen8<kGrad>(ldg_nt<u32x4>(gp[r], v));
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float x[4][N];
-#pragma unroll
-                    for (int r = 0; r < N; ++r)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e][r] = f[r][4 * hh + e];
-                    reduce_store<N>(x, out, 2 * static_cast<int64_t>(v) + hh, ss, bad);
-                }
-            }
-        }
-    }
-    for (int i = nvec * kVec + tid; i < len; i += kBlock) {
-        float x[N];
+    if (e0 + 4 <= q.len && ok) {
+        float x[4][N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            if constexpr (kMode == 0) x[r] = ldg<float>(ap[r], i);
-            else if constexpr (kMode == 1) x[r] = widen1<kGrad>(ldg<uint16_t>(gp[r], i));
-            else x[r] = ldg<float>(ap[r], i) + widen1<kGrad>(ldg<uint16_t>(gp[r], i));
+            f32x4 t;
+            if constexpr (kMode == 0) t = ldg_nt<f32x4>(ap[r], lane);
+            else if constexpr (kMode == 1) t = widen4<kGrad>(ldg_nt<u32x2>(gp[r], lane));
+            else t = ldg_nt<f32x4>(ap[r], lane) + widen4<kGrad>(ldg_nt<u32x2>(gp[r], lane));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e][r] = t[e];
         }
-        const float y = average<N>(tree_sum<N>(x));
-        stg<float>(out, i, y);
-        ss += static_cast<double>(y) * static_cast<double>(y);
-        bad += nonfinite(y);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            y[e] = average<N>(tree_sum<N>(x[e]));
+            add_stats(y[e], ss, bad);
+        }
+        stg_nt<f32x4>(out, lane, y);
+    } else {
+        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+            float x[N];
+#pragma unroll
+            for (int r = 0; r < N; ++r) {
+                if constexpr (kMode == 0) x[r] = ldg<float>(ap[r], i);
+                else if constexpr (kMode == 1) x[r] = widen1<kGrad>(ldg<uint16_t>(gp[r], i));
+                else x[r] = ldg<float>(ap[r], i) + widen1<kGrad>(ldg<uint16_t>(gp[r], i));
+            }
+            const float y = average<N>(tree_sum<N>(x));
+            stg<float>(out, i, y);
+            add_stats(y, ss, bad);
+        }
     }
-    block_stats_store(ss, bad, cid, sb);
+    wave_stats_store(ss, bad, p, sb);
 }
 
 // ============================================================================
 // statistics scan of gbar (when not fused into the producer)
 // ============================================================================
-__global__ void __launch_bounds__(kBlock) k_stats(const dp_chunk* __restrict__ chunks, int64_t base, RoleRef gbar,
-                                                    StatsBuf sb) {
-    const int64_t cid = base + blockIdx.x;
-    const dp_chunk c = chunks[cid];
-    const float* __restrict__ x = elem_ptr<const float>(gbar, c);
-    const int len = c.len, tid = threadIdx.x;
-    const int nvec = aligned16(x) ? (len >> 2) : 0;
+__global__ void __launch_bounds__(kWave) k_stats(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
+                                                   RoleRef gbar, StatsBuf sb) {
+    const int64_t p = base + blockIdx.x;
+    const Piece q = piece_of(chunks, p, log2s);
+    const float* __restrict__ x = elem_ptr<const float>(gbar, q);
+    const int lane = threadIdx.x, e0 = lane * 4;
     double ss = 0.0;
     uint32_t bad = 0;
-    for (int v = tid; v < nvec; v += kBlock) {
-        const f32x4 q = ldg_nt<f32x4>(x, v);
+    if (e0 + 4 <= q.len && aligned(x, 16)) {
+        const f32x4 v = ldg_nt<f32x4>(x, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ss += static_cast<double>(q[e]) * static_cast<double>(q[e]);
-            bad += nonfinite(q[e]);
-        }
+        for (int e = 0; e < 4; ++e) add_stats(v[e], ss, bad);
+    } else {
+        for (int i = e0; i < e0 + 4 && i < q.len; ++i) add_stats(ldg<float>(x, i), ss, bad);
     }
-    for (int i = nvec * 4 + tid; i < len; i += kBlock) {
-        const float y = ldg<float>(x, i);
-        ss += static_cast<double>(y) * static_cast<double>(y);
-        bad += nonfinite(y);
-    }
-    block_stats_store(ss, bad, cid, sb);
+    wave_stats_store(ss, bad, p, sb);
 }
 
 // ============================================================================
-// pass 2: the chunk partials are folded in a fixed order -- by groups of
+// pass 2: the piece partials are folded in a fixed order -- by groups of
 // kFoldGroup when there are many -- and one workgroup updates the scalar state
 // ============================================================================
 template <typename Count>
 __device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, const Count* __restrict__ bad_in,
                                            int64_t lo, int64_t hi, double& ss_out, uint64_t& bad_out) {
-    __shared__ double s_ss[kBlock];
-    __shared__ uint64_t s_bad[kBlock];
+    __shared__ double s_ss[kFoldThreads];
+    __shared__ uint64_t s_bad[kFoldThreads];
     const int tid = threadIdx.x;
     double ss = 0.0;
     uint64_t bad = 0;
-    for (int64_t i = lo + tid; i < hi; i += kBlock) {
+    for (int64_t i = lo + tid; i < hi; i += kFoldThreads) {
         ss += ss_in[i];
         bad += bad_in[i];
     }
     s_ss[tid] = ss;
     s_bad[tid] = bad;
     __syncthreads();
-    for (int w = kBlock / 2; w > 0; w >>= 1) {
+    for (int w = kFoldThreads / 2; w > 0; w >>= 1) {
         if (tid < w) {
             s_ss[tid] = s_ss[tid] + s_ss[tid + w];
             s_bad[tid] = s_bad[tid] + s_bad[tid + w];
@@ -405,7 +318,7 @@ __device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, con
     bad_out = s_bad[0];
 }
 
-__global__ void __launch_bounds__(kBlock) k_fold(StatsBuf sb, int64_t nparts, FoldBuf fold) {
+__global__ void __launch_bounds__(kFoldThreads) k_fold(StatsBuf sb, int64_t nparts, FoldBuf fold) {
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFoldGroup;
     const int64_t hi = lo + kFoldGroup < nparts ? lo + kFoldGroup : nparts;
     double ss;
@@ -418,8 +331,9 @@ __global__ void __launch_bounds__(kBlock) k_fold(StatsBuf sb, int64_t nparts, Fo
 }
 
 template <typename Count>
-__global__ void __launch_bounds__(kBlock) k_finalize(const double* __restrict__ ss_in, const Count* __restrict__ bad_in,
-                                                       int64_t nparts, DevState* __restrict__ st, ScalerArgs args) {
+__global__ void __launch_bounds__(kFoldThreads) k_finalize(const double* __restrict__ ss_in,
+                                                             const Count* __restrict__ bad_in, int64_t nparts,
+                                                             DevState* __restrict__ st, ScalerArgs args) {
     double sumsq;
     uint64_t badsum;
     block_fold(ss_in, bad_in, 0, nparts, sumsq, badsum);
@@ -496,9 +410,9 @@ __device__ __forceinline__ void adam1(float gb, float& w, float& m, float& v, co
 }
 
 template <int kParam>
-__global__ void __launch_bounds__(kBlock) k_adamw(const dp_chunk* __restrict__ chunks, int64_t base, RoleRef gbar,
-                                                    RoleRef wr, RoleRef mr, RoleRef vr, RoleRef pr,
-                                                    const DevState* __restrict__ st, AdamArgs args) {
+__global__ void __launch_bounds__(kWave) k_adamw(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
+                                                   RoleRef gbar, RoleRef wr, RoleRef mr, RoleRef vr, RoleRef pr,
+                                                   const DevState* __restrict__ st, AdamArgs args) {
     if (st->found_inf) return;
     AdamCoef k;
     {
@@ -513,67 +427,52 @@ __global__ void __launch_bounds__(kBlock) k_adamw(const dp_chunk* __restrict__ c
         k.eps = args.eps;
         k.dec = 1.0 - args.lr * args.weight_decay;
     }
-
-    const int64_t cid = base + blockIdx.x;
-    const dp_chunk c = chunks[cid];
-    const float* __restrict__ gp = elem_ptr<const float>(gbar, c);
-    float* __restrict__ wp = elem_ptr<float>(wr, c);
-    float* __restrict__ mp = elem_ptr<float>(mr, c);
-    float* __restrict__ vp = elem_ptr<float>(vr, c);
-    uint16_t* __restrict__ pp = elem_ptr<uint16_t>(pr, c);
-    const int len = c.len, tid = threadIdx.x;
-    const bool ok = aligned16(gp) && aligned16(wp) && aligned16(mp) && aligned16(vp) &&
-                    (reinterpret_cast<uintptr_t>(pp) & 7u) == 0;
-    const int nvec = ok ? (len >> 2) : 0;  // 4 elements per vector
-    constexpr int U = 2;
-    for (int v0 = 0; v0 < nvec; v0 += kBlock * U) {
-        f32x4 G[U], W[U], M[U], V[U];
+    const Piece q = piece_of(chunks, base + blockIdx.x, log2s);
+    const float* __restrict__ gp = elem_ptr<const float>(gbar, q);
+    float* __restrict__ wp = elem_ptr<float>(wr, q);
+    float* __restrict__ mp = elem_ptr<float>(mr, q);
+    float* __restrict__ vp = elem_ptr<float>(vr, q);
+    uint16_t* __restrict__ pp = elem_ptr<uint16_t>(pr, q);
+    const int lane = threadIdx.x, e0 = lane * 4;
+    if (e0 + 4 <= q.len && aligned(gp, 16) && aligned(wp, 16) && aligned(mp, 16) && aligned(vp, 16) &&
+        aligned(pp, 8)) {
+        const f32x4 G = ldg_nt<f32x4>(gp, lane);
+        const f32x4 W = ldg_nt<f32x4>(wp, lane);
+        const f32x4 M = ldg_nt<f32x4>(mp, lane);
+        const f32x4 V = ldg_nt<f32x4>(vp, lane);
+        float w4[4] = {W[0], W[1], W[2], W[3]};
+        float m4[4] = {M[0], M[1], M[2], M[3]};
+        float v4[4] = {V[0], V[1], V[2], V[3]};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int q = v0 + u * kBlock + tid;
-            if (q < nvec) {
-                G[u] = ldg_nt<f32x4>(gp, q);
-                W[u] = ldg_nt<f32x4>(wp, q);
-                M[u] = ldg_nt<f32x4>(mp, q);
-                V[u] = ldg_nt<f32x4>(vp, q);
-            }
+        for (int e = 0; e < 4; ++e) adam1(G[e], w4[e], m4[e], v4[e], k);
+        stg_nt<f32x4>(wp, lane, f32x4{w4[0], w4[1], w4[2], w4[3]});
+        stg_nt<f32x4>(mp, lane, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        stg_nt<f32x4>(vp, lane, f32x4{v4[0], v4[1], v4[2], v4[3]});
+        const uint32_t p01 = static_cast<uint32_t>(narrow1<kParam>(w4[0])) |
+                             (static_cast<uint32_t>(narrow1<kParam>(w4[1])) << 16);
+        const uint32_t p23 = static_cast<uint32_t>(narrow1<kParam>(w4[2])) |
+                             (static_cast<uint32_t>(narrow1<kParam>(w4[3])) << 16);
+        stg_nt<u32x2>(pp, lane, u32x2{p01, p23});
+    } else {
+        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+            float w = ldg<float>(wp, i), m = ldg<float>(mp, i), v = ldg<float>(vp, i);
+            adam1(ldg<float>(gp, i), w, m, v, k);
+            stg<float>(wp, i, w);
+            stg<float>(mp, i, m);
+            stg<float>(vp, i, v);
+            stg<uint16_t>(pp, i, narrow1<kParam>(w));
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int q = v0 + u * kBlock + tid;
-            if (q < nvec) {
-                float w4[4] = {W[u][0], W[u][1], W[u][2], W[u][3]};
-                float m4[4] = {M[u][0], M[u][1], M[u][2], M[u][3]};
-                float v4[4] = {V[u][0], V[u][1], V[u][2], V[u][3]};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) adam1(G[u][e], w4[e], m4[e], v4[e], k);
-                stg_nt<f32x4>(wp, q, f32x4{w4[0], w4[1], w4[2], w4[3]});
-                stg_nt<f32x4>(mp, q, f32x4{m4[0], m4[1], m4[2], m4[3]});
-                stg_nt<f32x4>(vp, q, f32x4{v4[0], v4[1], v4[2], v4[3]});
-                const uint32_t p01 = static_cast<uint32_t>(narrow1<kParam>(w4[0])) |
-                                     (static_cast<uint32_t>(narrow1<kParam>(w4[1])) << 16);
-                const uint32_t p23 = static_cast<uint32_t>(narrow1<kParam>(w4[2])) |
-                                     (static_cast<uint32_t>(narrow1<kParam>(w4[3])) << 16);
-                stg_nt<u32x2>(pp, q, u32x2{p01, p23});
-            }
-        }
-    }
-    for (int i = nvec * 4 + tid; i < len; i += kBlock) {
-        float w = ldg<float>(wp, i), m = ldg<float>(mp, i), v = ldg<float>(vp, i);
-        adam1(ldg<float>(gp, i), w, m, v, k);
-        stg<float>(wp, i, w);
-        stg<float>(mp, i, m);
-        stg<float>(vp, i, v);
-        stg<uint16_t>(pp, i, narrow1<kParam>(w));
     }
 }
 
 // ---- launch helpers ---------------------------------------------------------
+// Launches `launch(base, grid)` over npieces workgroups in slices of at most
+// kMaxBlocksPerLaunch (gridDim.y = ny).
 template <typename F>
-hipError_t for_pieces(int64_t nchunks, F&& launch) {
-    for (int64_t b = 0; b < nchunks; b += kMaxBlocksPerLaunch) {
-        const int64_t cnt = nchunks - b < kMaxBlocksPerLaunch ? nchunks - b : kMaxBlocksPerLaunch;
-        launch(b, dim3(static_cast<unsigned>(cnt)));
+hipError_t for_pieces(int64_t npieces, unsigned ny, F&& launch) {
+    for (int64_t b = 0; b < npieces; b += kMaxBlocksPerLaunch) {
+        const int64_t cnt = npieces - b < kMaxBlocksPerLaunch ? npieces - b : kMaxBlocksPerLaunch;
+        launch(b, dim3(static_cast<unsigned>(cnt), ny));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -581,19 +480,19 @@ hipError_t for_pieces(int64_t nchunks, F&& launch) {
 }
 
 template <int kMode, int kGrad, int N>
-hipError_t reduce_n(const dp_chunk* chunks, int64_t nchunks, const Srcs& accs, const Srcs& grads, RoleRef gbar,
-                    StatsBuf sb, hipStream_t s) {
-    return for_pieces(nchunks, [&](int64_t b, dim3 grid) {
-        hipLaunchKernelGGL((k_reduce<kMode, kGrad, N>), grid, dim3(kBlock), 0, s, chunks, b, accs, grads, gbar, sb);
+hipError_t reduce_n(const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+        hipLaunchKernelGGL((k_reduce<kMode, kGrad, N>), grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, accs, grads,
+                           gbar, sb);
     });
 }
 
 template <int kMode, int kGrad>
-hipError_t reduce_dispatch(int n, const dp_chunk* chunks, int64_t nchunks, const Srcs& accs, const Srcs& grads,
-                           RoleRef gbar, StatsBuf sb, hipStream_t s) {
+hipError_t reduce_dispatch(int n, const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb,
+                           hipStream_t s) {
     switch (n) {
 #define DP_CASE(K) \
-    case K: return reduce_n<kMode, kGrad, K>(chunks, nchunks, accs, grads, gbar, sb, s);
+    case K: return reduce_n<kMode, kGrad, K>(t, accs, grads, gbar, sb, s);
         DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
         DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
 #undef DP_CASE
@@ -603,11 +502,12 @@ hipError_t reduce_dispatch(int n, const dp_chunk* chunks, int64_t nchunks, const
 
 }  // namespace
 
-hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const dp_chunk* chunks, int64_t nchunks,
-                             RoleRef grad, RoleRef acc, StatsBuf sb, hipStream_t s) {
-    return for_pieces(nchunks, [&](int64_t b, dim3 grid) {
-        const dim3 blk(kBlock);
-#define DP_ACC(G, F, S) hipLaunchKernelGGL((k_accumulate<G, F, S>), grid, blk, 0, s, chunks, b, grad, acc, sb)
+hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
+                             StatsBuf sb, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+        const dim3 blk(kWave);
+#define DP_ACC(G, F, S) \
+    hipLaunchKernelGGL((k_accumulate<G, F, S>), grid, blk, 0, s, t.chunks, t.log2s, b, grad, acc, sb)
         if (gdt == DP_BF16) {
             if (first) { if (stats) DP_ACC(2, true, true); else DP_ACC(2, true, false); }
             else { if (stats) DP_ACC(2, false, true); else DP_ACC(2, false, false); }
@@ -619,63 +519,64 @@ hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const dp_chun
     });
 }
 
-hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const dp_chunk* chunks, int64_t nchunks,
-                                 const Srcs& grads, const Srcs& accs, hipStream_t s) {
-    return for_pieces(nchunks * n, [&](int64_t b, dim3 grid) {
-        const dim3 blk(kBlock);
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
+                                 hipStream_t s) {
+    return for_pieces(t.npieces, static_cast<unsigned>(n), [&](int64_t b, dim3 grid) {
+        const dim3 blk(kWave);
         if (gdt == DP_BF16) {
-            if (first) hipLaunchKernelGGL((k_accumulate_all<2, true>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
-            else hipLaunchKernelGGL((k_accumulate_all<2, false>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+            if (first) hipLaunchKernelGGL((k_accumulate_all<2, true>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
+            else hipLaunchKernelGGL((k_accumulate_all<2, false>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
         } else {
-            if (first) hipLaunchKernelGGL((k_accumulate_all<1, true>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
-            else hipLaunchKernelGGL((k_accumulate_all<1, false>), grid, blk, 0, s, chunks, nchunks, b, grads, accs);
+            if (first) hipLaunchKernelGGL((k_accumulate_all<1, true>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
+            else hipLaunchKernelGGL((k_accumulate_all<1, false>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
         }
     });
 }
 
-hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const dp_chunk* chunks, int64_t nchunks,
-                         const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<0, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
+                         RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<0, 2>(n, t, accs, grads, gbar, sb, s);
     if (mode == ReduceMode::kGradients) {
-        if (gdt == DP_F16) return reduce_dispatch<1, 1>(n, chunks, nchunks, accs, grads, gbar, sb, s);
-        return reduce_dispatch<1, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+        if (gdt == DP_F16) return reduce_dispatch<1, 1>(n, t, accs, grads, gbar, sb, s);
+        return reduce_dispatch<1, 2>(n, t, accs, grads, gbar, sb, s);
     }
-    if (gdt == DP_F16) return reduce_dispatch<2, 1>(n, chunks, nchunks, accs, grads, gbar, sb, s);
-    return reduce_dispatch<2, 2>(n, chunks, nchunks, accs, grads, gbar, sb, s);
+    if (gdt == DP_F16) return reduce_dispatch<2, 1>(n, t, accs, grads, gbar, sb, s);
+    return reduce_dispatch<2, 2>(n, t, accs, grads, gbar, sb, s);
 }
 
-hipError_t launch_stats(const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    return for_pieces(nchunks, [&](int64_t b, dim3 grid) {
-        hipLaunchKernelGGL(k_stats, grid, dim3(kBlock), 0, s, chunks, b, gbar, sb);
+hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+        hipLaunchKernelGGL(k_stats, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, sb);
     });
 }
 
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t s) {
     if (nparts <= kFoldGroup) {
-        hipLaunchKernelGGL(k_finalize<uint32_t>, dim3(1), dim3(kBlock), 0, s, sb.sumsq, sb.bad, nparts, st, args);
+        hipLaunchKernelGGL(k_finalize<uint32_t>, dim3(1), dim3(kFoldThreads), 0, s, sb.sumsq, sb.bad, nparts, st, args);
         return hipGetLastError();
     }
     const int64_t groups = (nparts + kFoldGroup - 1) / kFoldGroup;
-    hipLaunchKernelGGL(k_fold, dim3(static_cast<unsigned>(groups)), dim3(kBlock), 0, s, sb, nparts, fold);
+    hipLaunchKernelGGL(k_fold, dim3(static_cast<unsigned>(groups)), dim3(kFoldThreads), 0, s, sb, nparts, fold);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_finalize<uint64_t>, dim3(1), dim3(kBlock), 0, s, fold.sumsq, fold.bad, groups, st, args);
+    hipLaunchKernelGGL(k_finalize<uint64_t>, dim3(1), dim3(kFoldThreads), 0, s, fold.sumsq, fold.bad, groups, st,
+                       args);
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(dp_dtype pdt, const dp_chunk* chunks, int64_t nchunks, RoleRef gbar, RoleRef w, RoleRef m,
-                        RoleRef v, RoleRef p, const DevState* st, const AdamArgs& args, hipStream_t s) {
-    return for_pieces(nchunks, [&](int64_t b, dim3 grid) {
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
+                        const DevState* st, const AdamArgs& args, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
         if (pdt == DP_BF16)
-            hipLaunchKernelGGL(k_adamw<2>, grid, dim3(kBlock), 0, s, chunks, b, gbar, w, m, v, p, st, args);
+            hipLaunchKernelGGL(k_adamw<2>, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, w, m, v, p, st, args);
         else
-            hipLaunchKernelGGL(k_adamw<1>, grid, dim3(kBlock), 0, s, chunks, b, gbar, w, m, v, p, st, args);
+            hipLaunchKernelGGL(k_adamw<1>, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, w, m, v, p, st, args);
     });
 }
 
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_state_init, dim3(1), dim3(64), 0, s, st, scale);
+    hipLaunchKernelGGL(k_state_init, dim3(1), dim3(kWave), 0, s, st, scale);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ extern "C" {
 
 #define DP_ABI_VERSION 1
 #define DP_MAX_REPLICAS 16
-#define DP_DEFAULT_CHUNK 2048
+#define DP_DEFAULT_CHUNK 16384
 
 typedef enum dp_status {
     DP_OK = 0,
@@ -87,7 +87,7 @@ typedef struct dp_layout {
     const int64_t* numel;  /* host: [num_tensors], each >= 0 */
     dp_dtype grad_dtype;   /* DP_F16 or DP_BF16 */
     dp_dtype param_dtype;  /* DP_F16 or DP_BF16 */
-    int32_t chunk_elems;   /* 0 = DP_DEFAULT_CHUNK; else a multiple of 256 in [256, 2^26] */
+    int32_t chunk_elems;   /* 0 = DP_DEFAULT_CHUNK; else a power of two in [256, 2^26] */
     int32_t reserved;
 } dp_layout;
 

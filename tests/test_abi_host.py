@@ -35,7 +35,8 @@ def test_abi_version_and_status_strings():
 
 
 @pytest.mark.parametrize("kw", [dict(n_replicas=0), dict(n_replicas=17), dict(grad_dtype="f32"),
-                                dict(param_dtype="f32"), dict(chunk_elems=100), dict(chunk_elems=1 << 27)])
+                                dict(param_dtype="f32"), dict(chunk_elems=100), dict(chunk_elems=1 << 27),
+                                dict(chunk_elems=768)])
 def test_bad_layouts_rejected(kw):
     args = dict(numel=[10, 20], n_replicas=2, grad_dtype="bf16", param_dtype="bf16", chunk_elems=0)
     args.update(kw)
@@ -85,8 +86,8 @@ def test_chunk_table_of_a_2pow32_tensor_uses_64bit_indices():
         mid = p.chunks((1 << 31) + 5, (1 << 31) + 70000)
         assert int(mid[0]["offset"]) == (1 << 31) + 5 and int(mid[0]["len"]) == 65531
     with dp.Plan((1 << 32,), 1, "bf16", "bf16") as p:
-        assert p.info()["chunk_elems"] == dp.DP_DEFAULT_CHUNK == 2048
-        assert p.info()["num_chunks"] == (1 << 32) // 2048
+        assert p.info()["chunk_elems"] == dp.DP_DEFAULT_CHUNK == 16384
+        assert p.info()["num_chunks"] == (1 << 32) // 16384
 
 
 def test_plan_info_byte_model():
