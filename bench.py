@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=1 << 22, help="params in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
+    ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
+                    help="bind the state as flat buffers, or through per-tensor pointer tables (same memory)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -129,7 +131,7 @@ def launch_bytes(w, kind: str) -> float:
     return w.P * per[kind] / launches.get(kind, 1)
 
 
-def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0):
+def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat"):
     import torch
 
     import synth
@@ -150,6 +152,20 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0):
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
+    if bind == "tensors":
+        # the same buffers, bound through per-tensor pointer tables
+        off = [int(x) for x in w.offsets[:-1]]
+
+        def per_tensor(t):
+            return [t.data_ptr() + o * t.element_size() for o in off]
+
+        for role, t in (("master", d.master), ("exp_avg", d.exp_avg), ("exp_avg_sq", d.exp_avg_sq),
+                        ("param", d.param)):
+            d.plan.bind_tensors(role, per_tensor(t))
+        for r, t in enumerate(d.acc):
+            d.plan.bind_tensors("acc", per_tensor(t), r)
+        if not (w.n == 1 and not w.partials):
+            d.plan.bind_tensors("gbar", per_tensor(d.gbar))
 
     # one batch of gradients, resident before the timed region
     calls = [(r, 1) for r in range(w.n)] if w.partials else [(r, k) for k in range(1, w.a + 1) for r in range(w.n)]
@@ -261,7 +277,7 @@ def main():
         print(json.dumps(res, indent=1))
         return
     w = workloads.by_name(args.workload)
-    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration)
+    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration, args.bind)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w)
     step_bytes = sum(per_param.values()) * w.P
@@ -297,7 +313,7 @@ def main():
                    "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "state": "fp32 master/m/v",
                    "update_arithmetic": "f64", "clip": w.max_norm, "loss_scale": w.scaler,
                    "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)",
-                   "chunk_elems": args.chunk or 2048},
+                   "chunk_elems": args.chunk or 16384, "binding": args.bind},
         "hbm_gbps": hbm_gbps,
         "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
         "bytes_per_param_step": sum(per_param.values()),

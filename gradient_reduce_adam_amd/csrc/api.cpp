@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -48,8 +49,14 @@ struct DeviceTable {
     dp_chunk* dev = nullptr;
     int log2s = 0;
 
-    int64_t npieces() const { return count << log2s; }
-    dpk::Table table() const { return dpk::Table{dev, npieces(), log2s}; }
+    // pieces of a launch over this range: direct flat pieces when every role
+    // of the call is flat-bound, else pieces of the chunks
+    int64_t npieces(bool flat) const {
+        if (!flat) return count << log2s;
+        const int64_t lo = begin & ~int64_t{3};
+        return end > begin ? (end - lo + dpk::kPiece - 1) / dpk::kPiece : 0;
+    }
+    dpk::Table table(bool flat) const { return dpk::Table{dev, begin, end, npieces(flat), log2s, flat}; }
 };
 
 int log2_exact(int64_t x) {
@@ -82,7 +89,8 @@ struct dp_plan {
     bool state_ready = false;
     dp_state_cfg cfg{};
     std::vector<int32_t> micro;   // micro-steps accumulated per replica since the last reduction
-    bool partials_valid = false;  // chunk statistics of the current g_bar exist
+    bool partials_valid = false;  // piece statistics of the current g_bar exist
+    int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
     bool stats_current = false;   // dp_grad_stats ran on the current g_bar
 };
 
@@ -182,6 +190,18 @@ dp_status need(const Binding* b, const char* what) {
 }
 
 dp_status check_launch(hipError_t e, const char* what) { return e == hipSuccess ? DP_OK : hip_fail(e, what); }
+
+bool all_flat(std::initializer_list<dpk::RoleRef> refs) {
+    for (const dpk::RoleRef& r : refs)
+        if (r.tab) return false;
+    return true;
+}
+
+bool all_flat(const dpk::Srcs& s, int n) {
+    for (int i = 0; i < n; ++i)
+        if (s.r[i].tab) return false;
+    return true;
+}
 
 }  // namespace
 
@@ -376,7 +396,8 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     if (!p->state) {
         hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->state), sizeof(dpk::DevState));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of the state block: %s", hipGetErrorString(e));
-        const size_t np = static_cast<size_t>(std::max<int64_t>(p->full.npieces(), 1));
+        const size_t np = static_cast<size_t>(
+            std::max<int64_t>(std::max(p->full.npieces(true), p->full.npieces(false)), 1));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.sumsq), np * sizeof(double));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
@@ -418,15 +439,17 @@ dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit
         return fail(DP_ERR_STATE, "replica %d: first == 0 without a first micro-step since the last reduction", replica);
     s = ensure_full(p);
     if (s != DP_OK) return s;
-    if (p->full.count > 0) {
-        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, p->full.table(), g.ref(), a.ref(),
-                                                p->stats, stream),
+    const dpk::Table t = p->full.table(first && !emit_stats && all_flat({g.ref(), a.ref()}));
+    if (t.npieces > 0) {
+        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, t, g.ref(), a.ref(), p->stats,
+                                                stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
     p->micro[replica] = first ? 1 : p->micro[replica] + 1;
     p->stats_current = false;
     p->partials_valid = emit_stats != 0;
+    p->partials_count = t.npieces;
     return DP_OK;
 }
 
@@ -446,14 +469,15 @@ static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs
     if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
     dp_status s = ensure_full(p);
     if (s != DP_OK) return s;
-    if (p->full.count > 0) {
-        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, p->full.table(), accs, grads, gb->ref(), p->stats,
-                                            stream),
+    const dpk::Table t = p->full.table(false);  // statistics: table pieces
+    if (t.npieces > 0) {
+        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, accs, grads, gb->ref(), p->stats, stream),
                          "reduce launch");
         if (s != DP_OK) return s;
     }
     std::fill(p->micro.begin(), p->micro.end(), 0);
     p->partials_valid = true;
+    p->partials_count = t.npieces;
     p->stats_current = false;
     return DP_OK;
 }
@@ -491,8 +515,17 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     }
     s = ensure_full(p);
     if (s != DP_OK) return s;
-    if (p->full.count > 0) {
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.table(), grads, accs, stream),
+    // Addressing (flat pieces or chunk-table pieces, see kernels.hip), as
+    // measured on MI355X: micro-steps after the first (read-modify-write of
+    // the accumulators) always go through the chunk table -- the table load
+    // each wave does before its first access staggers the waves' start and
+    // moves 7-8% more bytes per second on this pass -- while the write-mostly
+    // first micro-step is 15% faster on flat pieces.  Every kernel that
+    // writes statistics uses table pieces, so the summation order of the
+    // statistics does not depend on how the roles are bound.
+    const dpk::Table t = p->full.table(first && all_flat(grads, p->n) && all_flat(accs, p->n));
+    if (t.npieces > 0) {
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, grads, accs, stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
@@ -531,16 +564,19 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
         const Binding* gb = gbar_binding(p);
         s = need(gb, "GBAR");
         if (s != DP_OK) return s;
-        if (p->full.count > 0) {
-            s = check_launch(dpk::launch_stats(p->full.table(), gb->ref(), p->stats, stream), "stats launch");
+        const dpk::Table t = p->full.table(false);  // statistics: table pieces
+        if (t.npieces > 0) {
+            s = check_launch(dpk::launch_stats(t, gb->ref(), p->stats, stream), "stats launch");
             if (s != DP_OK) return s;
         }
+        p->partials_count = t.npieces;
     } else if (!p->partials_valid && p->full.count > 0) {
         return fail(DP_ERR_STATE, "no fused statistics for the current g_bar: reduce first, or pass scan = 1");
     }
     dpk::ScalerArgs a{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, max_norm,
                       p->cfg.scaler_mode, p->cfg.growth_interval};
-    s = check_launch(dpk::launch_finalize(p->stats, p->full.npieces(), p->fold, p->state, a, stream), "finalize launch");
+    const int64_t nparts = p->full.count > 0 ? p->partials_count : 0;
+    s = check_launch(dpk::launch_finalize(p->stats, nparts, p->fold, p->state, a, stream), "finalize launch");
     if (s != DP_OK) return s;
     p->partials_valid = false;
     p->stats_current = true;
@@ -568,9 +604,10 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
     s = range_table(p, begin, end, &t);
     if (s != DP_OK) return s;
     dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
-    return check_launch(dpk::launch_adamw(p->pdt, t->table(), gb->ref(), p->roles[DP_ROLE_MASTER][0].ref(),
-                                          p->roles[DP_ROLE_EXP_AVG][0].ref(), p->roles[DP_ROLE_EXP_AVG_SQ][0].ref(),
-                                          p->roles[DP_ROLE_PARAM][0].ref(), p->state, a, stream),
+    const dpk::RoleRef w = p->roles[DP_ROLE_MASTER][0].ref(), m = p->roles[DP_ROLE_EXP_AVG][0].ref(),
+                       v = p->roles[DP_ROLE_EXP_AVG_SQ][0].ref(), pr = p->roles[DP_ROLE_PARAM][0].ref();
+    return check_launch(dpk::launch_adamw(p->pdt, t->table(all_flat({gb->ref(), w, m, v, pr})), gb->ref(), w, m, v, pr,
+                                          p->state, a, stream),
                         "adamw launch");
 }
 

@@ -14,13 +14,18 @@ constexpr int kPiece = 4 * kWave;         // elements per streaming workgroup: 4
 constexpr int kFoldThreads = 256;         // threads of the statistics fold workgroups
 constexpr int64_t kMaxBlocksPerLaunch = int64_t{1} << 24;  // keeps gridDim.x * kWave below 2^32
 
-// A chunk table on the device, as the kernels see it: npieces = chunks << log2s
-// single-wave pieces of kPiece elements (the last pieces of a short chunk are
-// empty).
+// The pieces of one call's range [begin, end), as the kernels see them.
+//  flat:  every role of the call is one flat buffer; piece p covers flat
+//         elements [floor4(begin) + p * kPiece, ... + kPiece) within the range
+//  table: the chunk table of the range; npieces = chunks << log2s, piece p is
+//         piece (p & (2^log2s - 1)) of chunk (p >> log2s) (pieces past a short
+//         chunk's end are empty)
 struct Table {
     const dp_chunk* chunks;
+    int64_t begin, end;
     int64_t npieces;
     int log2s;  // log2(chunk_elems / kPiece)
+    bool flat;
 };
 
 // Where one role's memory is: a flat base (tensor i at element prefix[i]) or

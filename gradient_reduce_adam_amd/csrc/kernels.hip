@@ -1,12 +1,20 @@
 // gfx950 kernels of the data-parallel gradient reduce + AdamW step.
 //
-// Work decomposition.  The plan's chunk table splits the flat parameter space
-// into chunks of at most chunk_elems elements, each inside one tensor (so a
-// chunk keeps its tensor's alignment).  Every streaming kernel runs one wave64
-// workgroup per 256-element piece of a chunk: piece p is piece (p & (S-1)) of
-// chunk (p >> log2 S), S = chunk_elems / 256.  A lane moves 4 consecutive
-// elements, so each binary32 stream is one 16-byte access per lane and one
-// contiguous KiB per wave, and a 16-bit stream one 8-byte access per lane.
+// Work decomposition.  Every streaming kernel runs one wave64 workgroup per
+// 256-element piece.  A lane moves 4 consecutive elements, so each binary32
+// stream is one 16-byte access per lane and one contiguous KiB per wave, and a
+// 16-bit stream one 8-byte access per lane.  Pieces are found in one of two
+// ways:
+//  - flat (every role of the call bound as one flat buffer): piece p covers
+//    flat elements [lo, lo + 256) with lo = floor4(begin) + 256 p, clipped to
+//    [begin, end); no table is read, so the first memory access of a wave
+//    depends on nothing but its indices;
+//  - table: the plan's chunk table splits the range into chunks of at most
+//    chunk_elems elements inside one tensor, and piece p is piece (p & (S-1))
+//    of chunk (p >> log2 S), S = chunk_elems / 256.  Needed when a role is
+//    bound per tensor; also used for every kernel that writes statistics (so
+//    their summation order does not depend on the bindings) and for the
+//    read-modify-write accumulation (see api.cpp for the measurements).
 // Thousands of one-shot single-wave workgroups keep the addresses in flight
 // dense and spread over all HBM channels; measured on MI355X this beats
 // larger workgroups and persistent grid-stride loops by 10-25% on these
@@ -53,25 +61,59 @@ __device__ __forceinline__ bool aligned(const void* p, uintptr_t bytes) {
 }
 
 // ---- the piece a workgroup owns ----------------------------------------------
+// Element i of the piece (0 <= i < kPiece) is at offset i from the piece's
+// pointers; elements [vlo, vhi) belong to the call's range.
 struct Piece {
-    dp_chunk c;  // its chunk
-    int start;   // first element of the piece inside the chunk
-    int len;     // elements of the piece (0 .. kPiece)
+    int32_t tensor;  // table mode: tensor of the chunk
+    int64_t flat;    // flat index of element 0
+    int64_t offset;  // table mode: index of element 0 inside its tensor
+    int vlo, vhi;
 };
 
-__device__ __forceinline__ Piece piece_of(const dp_chunk* __restrict__ chunks, int64_t p, int log2s) {
+template <bool kFlat>
+__device__ __forceinline__ Piece piece_of(const Table& t, int64_t p) {
     Piece q;
-    q.c = chunks[p >> log2s];
-    q.start = static_cast<int>(p & ((int64_t{1} << log2s) - 1)) * kPiece;
-    const int rest = q.c.len - q.start;
-    q.len = rest < 0 ? 0 : (rest < kPiece ? rest : kPiece);
+    if constexpr (kFlat) {
+        const int64_t lo = (t.begin & ~int64_t{3}) + p * kPiece;
+        q.tensor = 0;
+        q.flat = lo;
+        q.offset = 0;
+        q.vlo = t.begin > lo ? static_cast<int>(t.begin - lo) : 0;
+        const int64_t rest = t.end - lo;
+        q.vhi = rest < kPiece ? static_cast<int>(rest) : kPiece;
+    } else {
+        const dp_chunk c = t.chunks[p >> t.log2s];
+        const int start = static_cast<int>(p & ((int64_t{1} << t.log2s) - 1)) * kPiece;
+        q.tensor = c.tensor;
+        q.flat = c.flat + start;
+        q.offset = c.offset + start;
+        q.vlo = 0;
+        const int rest = c.len - start;
+        q.vhi = rest < 0 ? 0 : (rest < kPiece ? rest : kPiece);
+    }
     return q;
 }
 
 template <typename T>
 __device__ __forceinline__ T* elem_ptr(const RoleRef& r, const Piece& q) {
-    if (r.tab) return static_cast<T*>(r.tab[q.c.tensor]) + q.c.offset + q.start;
-    return static_cast<T*>(r.base) + q.c.flat + q.start;
+    if (r.tab) return static_cast<T*>(r.tab[q.tensor]) + q.offset;
+    return static_cast<T*>(r.base) + q.flat;
+}
+
+// The 4 elements of this lane: all in range (vector path) or the in-range
+// subset [lo, hi) of [e0, e0 + 4) (per-element path).
+struct LaneSpan {
+    int e0, lo, hi;
+    bool full;
+};
+
+__device__ __forceinline__ LaneSpan lane_span(const Piece& q) {
+    LaneSpan l;
+    l.e0 = static_cast<int>(threadIdx.x) * 4;
+    l.lo = l.e0 > q.vlo ? l.e0 : q.vlo;
+    l.hi = l.e0 + 4 < q.vhi ? l.e0 + 4 : q.vhi;
+    l.full = l.e0 >= q.vlo && l.e0 + 4 <= q.vhi;
+    return l;
 }
 
 // ---- low-precision formats --------------------------------------------------
@@ -159,8 +201,9 @@ __device__ __forceinline__ void accumulate_piece(const Piece& q, RoleRef grad, R
                                                  uint32_t& bad) {
     const uint16_t* __restrict__ g = elem_ptr<const uint16_t>(grad, q);
     float* __restrict__ a = elem_ptr<float>(acc, q);
-    const int lane = threadIdx.x, e0 = lane * 4;
-    if (e0 + 4 <= q.len && aligned(g, 8) && aligned(a, 16)) {
+    const LaneSpan l = lane_span(q);
+    if (l.full && aligned(g, 8) && aligned(a, 16)) {
+        const int lane = threadIdx.x;
         f32x4 r = widen4<kGrad>(ldg_nt<u32x2>(g, lane));
         if constexpr (!kFirst) r = ldg<f32x4>(a, lane) + r;
         stg<f32x4>(a, lane, r);
@@ -169,7 +212,7 @@ __device__ __forceinline__ void accumulate_piece(const Piece& q, RoleRef grad, R
             for (int e = 0; e < 4; ++e) add_stats(r[e], ss, bad);
         }
     } else {
-        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+        for (int i = l.lo; i < l.hi; ++i) {
             const float gi = widen1<kGrad>(ldg<uint16_t>(g, i));
             const float r = kFirst ? gi : ldg<float>(a, i) + gi;
             stg<float>(a, i, r);
@@ -179,11 +222,10 @@ __device__ __forceinline__ void accumulate_piece(const Piece& q, RoleRef grad, R
 }
 
 // one replica; with kStats the piece statistics of the result (n = 1: it is g_bar)
-template <int kGrad, bool kFirst, bool kStats>
-__global__ void __launch_bounds__(kWave) k_accumulate(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
-                                                        RoleRef grad, RoleRef acc, StatsBuf sb) {
+template <bool kFlat, int kGrad, bool kFirst, bool kStats>
+__global__ void __launch_bounds__(kWave) k_accumulate(Table t, int64_t base, RoleRef grad, RoleRef acc, StatsBuf sb) {
     const int64_t p = base + blockIdx.x;
-    const Piece q = piece_of(chunks, p, log2s);
+    const Piece q = piece_of<kFlat>(t, p);
     double ss = 0.0;
     uint32_t bad = 0;
     accumulate_piece<kGrad, kFirst, kStats>(q, grad, acc, ss, bad);
@@ -192,10 +234,9 @@ __global__ void __launch_bounds__(kWave) k_accumulate(const dp_chunk* __restrict
 
 // every replica's micro-step in one launch: blockIdx.y is the replica (the
 // dispatcher walks x fastest, so each replica's buffers stream in order)
-template <int kGrad, bool kFirst>
-__global__ void __launch_bounds__(kWave) k_accumulate_all(const dp_chunk* __restrict__ chunks, int log2s,
-                                                            int64_t base, Srcs grads, Srcs accs) {
-    const Piece q = piece_of(chunks, base + blockIdx.x, log2s);
+template <bool kFlat, int kGrad, bool kFirst>
+__global__ void __launch_bounds__(kWave) k_accumulate_all(Table t, int64_t base, Srcs grads, Srcs accs) {
+    const Piece q = piece_of<kFlat>(t, base + blockIdx.x);
     double ss = 0.0;
     uint32_t bad = 0;
     accumulate_piece<kGrad, kFirst, false>(q, grads.r[blockIdx.y], accs.r[blockIdx.y], ss, bad);
@@ -208,11 +249,11 @@ __global__ void __launch_bounds__(kWave) k_accumulate_all(const dp_chunk* __rest
 //   kMode 2: x_r = acc_r + g_r           (the last micro-step fused: acc_r is
 //                                         not written back)
 // ============================================================================
-template <int kMode, int kGrad, int N>
-__global__ void __launch_bounds__(kWave) k_reduce(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
-                                                    Srcs accs, Srcs grads, RoleRef gbar, StatsBuf sb) {
+template <bool kFlat, int kMode, int kGrad, int N>
+__global__ void __launch_bounds__(kWave) k_reduce(Table t, int64_t base, Srcs accs, Srcs grads, RoleRef gbar,
+                                                    StatsBuf sb) {
     const int64_t p = base + blockIdx.x;
-    const Piece q = piece_of(chunks, p, log2s);
+    const Piece q = piece_of<kFlat>(t, p);
     const float* ap[N];
     const uint16_t* gp[N];
     bool ok = true;
@@ -229,10 +270,11 @@ __global__ void __launch_bounds__(kWave) k_reduce(const dp_chunk* __restrict__ c
     }
     float* __restrict__ out = elem_ptr<float>(gbar, q);
     ok = ok && aligned(out, 16);
-    const int lane = threadIdx.x, e0 = lane * 4;
+    const int lane = threadIdx.x;
+    const LaneSpan l = lane_span(q);
     double ss = 0.0;
     uint32_t bad = 0;
-    if (e0 + 4 <= q.len && ok) {
+    if (l.full && ok) {
         float x[4][N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
@@ -251,7 +293,7 @@ __global__ void __launch_bounds__(kWave) k_reduce(const dp_chunk* __restrict__ c
         }
         stg_nt<f32x4>(out, lane, y);
     } else {
-        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+        for (int i = l.lo; i < l.hi; ++i) {
             float x[N];
 #pragma unroll
             for (int r = 0; r < N; ++r) {
@@ -270,20 +312,20 @@ __global__ void __launch_bounds__(kWave) k_reduce(const dp_chunk* __restrict__ c
 // ============================================================================
 // statistics scan of gbar (when not fused into the producer)
 // ============================================================================
-__global__ void __launch_bounds__(kWave) k_stats(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
-                                                   RoleRef gbar, StatsBuf sb) {
+template <bool kFlat>
+__global__ void __launch_bounds__(kWave) k_stats(Table t, int64_t base, RoleRef gbar, StatsBuf sb) {
     const int64_t p = base + blockIdx.x;
-    const Piece q = piece_of(chunks, p, log2s);
+    const Piece q = piece_of<kFlat>(t, p);
     const float* __restrict__ x = elem_ptr<const float>(gbar, q);
-    const int lane = threadIdx.x, e0 = lane * 4;
+    const LaneSpan l = lane_span(q);
     double ss = 0.0;
     uint32_t bad = 0;
-    if (e0 + 4 <= q.len && aligned(x, 16)) {
-        const f32x4 v = ldg_nt<f32x4>(x, lane);
+    if (l.full && aligned(x, 16)) {
+        const f32x4 v = ldg_nt<f32x4>(x, threadIdx.x);
 #pragma unroll
         for (int e = 0; e < 4; ++e) add_stats(v[e], ss, bad);
     } else {
-        for (int i = e0; i < e0 + 4 && i < q.len; ++i) add_stats(ldg<float>(x, i), ss, bad);
+        for (int i = l.lo; i < l.hi; ++i) add_stats(ldg<float>(x, i), ss, bad);
     }
     wave_stats_store(ss, bad, p, sb);
 }
@@ -409,10 +451,10 @@ __device__ __forceinline__ void adam1(float gb, float& w, float& m, float& v, co
     w = static_cast<float>(wi);
 }
 
-template <int kParam>
-__global__ void __launch_bounds__(kWave) k_adamw(const dp_chunk* __restrict__ chunks, int log2s, int64_t base,
-                                                   RoleRef gbar, RoleRef wr, RoleRef mr, RoleRef vr, RoleRef pr,
-                                                   const DevState* __restrict__ st, AdamArgs args) {
+template <bool kFlat, int kParam>
+__global__ void __launch_bounds__(kWave) k_adamw(Table t, int64_t base, RoleRef gbar, RoleRef wr, RoleRef mr,
+                                                   RoleRef vr, RoleRef pr, const DevState* __restrict__ st,
+                                                   AdamArgs args) {
     if (st->found_inf) return;
     AdamCoef k;
     {
@@ -427,15 +469,15 @@ __global__ void __launch_bounds__(kWave) k_adamw(const dp_chunk* __restrict__ ch
         k.eps = args.eps;
         k.dec = 1.0 - args.lr * args.weight_decay;
     }
-    const Piece q = piece_of(chunks, base + blockIdx.x, log2s);
+    const Piece q = piece_of<kFlat>(t, base + blockIdx.x);
     const float* __restrict__ gp = elem_ptr<const float>(gbar, q);
     float* __restrict__ wp = elem_ptr<float>(wr, q);
     float* __restrict__ mp = elem_ptr<float>(mr, q);
     float* __restrict__ vp = elem_ptr<float>(vr, q);
     uint16_t* __restrict__ pp = elem_ptr<uint16_t>(pr, q);
-    const int lane = threadIdx.x, e0 = lane * 4;
-    if (e0 + 4 <= q.len && aligned(gp, 16) && aligned(wp, 16) && aligned(mp, 16) && aligned(vp, 16) &&
-        aligned(pp, 8)) {
+    const int lane = threadIdx.x;
+    const LaneSpan l = lane_span(q);
+    if (l.full && aligned(gp, 16) && aligned(wp, 16) && aligned(mp, 16) && aligned(vp, 16) && aligned(pp, 8)) {
         const f32x4 G = ldg_nt<f32x4>(gp, lane);
         const f32x4 W = ldg_nt<f32x4>(wp, lane);
         const f32x4 M = ldg_nt<f32x4>(mp, lane);
@@ -454,7 +496,7 @@ __global__ void __launch_bounds__(kWave) k_adamw(const dp_chunk* __restrict__ ch
                              (static_cast<uint32_t>(narrow1<kParam>(w4[3])) << 16);
         stg_nt<u32x2>(pp, lane, u32x2{p01, p23});
     } else {
-        for (int i = e0; i < e0 + 4 && i < q.len; ++i) {
+        for (int i = l.lo; i < l.hi; ++i) {
             float w = ldg<float>(wp, i), m = ldg<float>(mp, i), v = ldg<float>(vp, i);
             adam1(ldg<float>(gp, i), w, m, v, k);
             stg<float>(wp, i, w);
@@ -479,20 +521,19 @@ hipError_t for_pieces(int64_t npieces, unsigned ny, F&& launch) {
     return hipSuccess;
 }
 
-template <int kMode, int kGrad, int N>
+template <bool kFlat, int kMode, int kGrad, int N>
 hipError_t reduce_n(const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
     return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
-        hipLaunchKernelGGL((k_reduce<kMode, kGrad, N>), grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, accs, grads,
-                           gbar, sb);
+        hipLaunchKernelGGL((k_reduce<kFlat, kMode, kGrad, N>), grid, dim3(kWave), 0, s, t, b, accs, grads, gbar, sb);
     });
 }
 
-template <int kMode, int kGrad>
+template <bool kFlat, int kMode, int kGrad>
 hipError_t reduce_dispatch(int n, const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb,
                            hipStream_t s) {
     switch (n) {
 #define DP_CASE(K) \
-    case K: return reduce_n<kMode, kGrad, K>(t, accs, grads, gbar, sb, s);
+    case K: return reduce_n<kFlat, kMode, kGrad, K>(t, accs, grads, gbar, sb, s);
         DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
         DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
 #undef DP_CASE
@@ -500,15 +541,27 @@ hipError_t reduce_dispatch(int n, const Table& t, const Srcs& accs, const Srcs& 
     }
 }
 
-}  // namespace
+template <bool kFlat>
+hipError_t reduce_modes(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
+                        RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<kFlat, 0, 2>(n, t, accs, grads, gbar, sb, s);
+    if (mode == ReduceMode::kGradients) {
+        if (gdt == DP_F16) return reduce_dispatch<kFlat, 1, 1>(n, t, accs, grads, gbar, sb, s);
+        return reduce_dispatch<kFlat, 1, 2>(n, t, accs, grads, gbar, sb, s);
+    }
+    if (gdt == DP_F16) return reduce_dispatch<kFlat, 2, 1>(n, t, accs, grads, gbar, sb, s);
+    return reduce_dispatch<kFlat, 2, 2>(n, t, accs, grads, gbar, sb, s);
+}
 
-hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
-                             StatsBuf sb, hipStream_t s) {
+template <bool kFlat>
+hipError_t accumulate_t(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc, StatsBuf sb,
+                        hipStream_t s) {
     return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
         const dim3 blk(kWave);
-#define DP_ACC(G, F, S) \
-    hipLaunchKernelGGL((k_accumulate<G, F, S>), grid, blk, 0, s, t.chunks, t.log2s, b, grad, acc, sb)
-        if (gdt == DP_BF16) {
+#define DP_ACC(G, F, S) hipLaunchKernelGGL((k_accumulate<kFlat, G, F, S>), grid, blk, 0, s, t, b, grad, acc, sb)
+        if constexpr (kFlat) {
+            if (gdt == DP_BF16) DP_ACC(2, true, false); else DP_ACC(1, true, false);
+        } else if (gdt == DP_BF16) {
             if (first) { if (stats) DP_ACC(2, true, true); else DP_ACC(2, true, false); }
             else { if (stats) DP_ACC(2, false, true); else DP_ACC(2, false, false); }
         } else {
@@ -519,34 +572,62 @@ hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& 
     });
 }
 
-hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
-                                 hipStream_t s) {
+template <bool kFlat>
+hipError_t accumulate_all_t(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
+                            hipStream_t s) {
     return for_pieces(t.npieces, static_cast<unsigned>(n), [&](int64_t b, dim3 grid) {
         const dim3 blk(kWave);
-        if (gdt == DP_BF16) {
-            if (first) hipLaunchKernelGGL((k_accumulate_all<2, true>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
-            else hipLaunchKernelGGL((k_accumulate_all<2, false>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
+#define DP_ALL(G, F) hipLaunchKernelGGL((k_accumulate_all<kFlat, G, F>), grid, blk, 0, s, t, b, grads, accs)
+        if constexpr (kFlat) {
+            if (gdt == DP_BF16) DP_ALL(2, true); else DP_ALL(1, true);
+        } else if (gdt == DP_BF16) {
+            if (first) DP_ALL(2, true); else DP_ALL(2, false);
         } else {
-            if (first) hipLaunchKernelGGL((k_accumulate_all<1, true>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
-            else hipLaunchKernelGGL((k_accumulate_all<1, false>), grid, blk, 0, s, t.chunks, t.log2s, b, grads, accs);
+            if (first) DP_ALL(1, true); else DP_ALL(1, false);
         }
+#undef DP_ALL
     });
+}
+
+template <bool kFlat>
+hipError_t adamw_t(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
+                   const DevState* st, const AdamArgs& args, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+        if (pdt == DP_BF16)
+            hipLaunchKernelGGL((k_adamw<kFlat, 2>), grid, dim3(kWave), 0, s, t, b, gbar, w, m, v, p, st, args);
+        else
+            hipLaunchKernelGGL((k_adamw<kFlat, 1>), grid, dim3(kWave), 0, s, t, b, gbar, w, m, v, p, st, args);
+    });
+}
+
+}  // namespace
+
+// Flat pieces serve only the first micro-step (no statistics) and the update;
+// everything else runs on table pieces (the host decides, see api.cpp).
+hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
+                             StatsBuf sb, hipStream_t s) {
+    if (t.flat && (!first || stats)) return hipErrorInvalidValue;
+    return t.flat ? accumulate_t<true>(gdt, true, false, t, grad, acc, sb, s)
+                  : accumulate_t<false>(gdt, first, stats, t, grad, acc, sb, s);
+}
+
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
+                                 hipStream_t s) {
+    if (t.flat && !first) return hipErrorInvalidValue;
+    return t.flat ? accumulate_all_t<true>(gdt, true, n, t, grads, accs, s)
+                  : accumulate_all_t<false>(gdt, first, n, t, grads, accs, s);
 }
 
 hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
                          RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<0, 2>(n, t, accs, grads, gbar, sb, s);
-    if (mode == ReduceMode::kGradients) {
-        if (gdt == DP_F16) return reduce_dispatch<1, 1>(n, t, accs, grads, gbar, sb, s);
-        return reduce_dispatch<1, 2>(n, t, accs, grads, gbar, sb, s);
-    }
-    if (gdt == DP_F16) return reduce_dispatch<2, 1>(n, t, accs, grads, gbar, sb, s);
-    return reduce_dispatch<2, 2>(n, t, accs, grads, gbar, sb, s);
+    if (t.flat) return hipErrorInvalidValue;
+    return reduce_modes<false>(mode, gdt, n, t, accs, grads, gbar, sb, s);
 }
 
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (t.flat) return hipErrorInvalidValue;
     return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
-        hipLaunchKernelGGL(k_stats, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, sb);
+        hipLaunchKernelGGL(k_stats<false>, grid, dim3(kWave), 0, s, t, b, gbar, sb);
     });
 }
 
@@ -567,12 +648,8 @@ hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* 
 
 hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
                         const DevState* st, const AdamArgs& args, hipStream_t s) {
-    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
-        if (pdt == DP_BF16)
-            hipLaunchKernelGGL(k_adamw<2>, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, w, m, v, p, st, args);
-        else
-            hipLaunchKernelGGL(k_adamw<1>, grid, dim3(kWave), 0, s, t.chunks, t.log2s, b, gbar, w, m, v, p, st, args);
-    });
+    return t.flat ? adamw_t<true>(pdt, t, gbar, w, m, v, p, st, args, s)
+                  : adamw_t<false>(pdt, t, gbar, w, m, v, p, st, args, s);
 }
 
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t s) {
