@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 RESIDENT_GRAD_BUDGET = 80e9  # bytes of pre-generated gradients kept in HBM
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip")
+KERNEL_SRC = (os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip"),
+              os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "dp_internal.h"))
 
 
 def parse():
@@ -52,12 +53,13 @@ def parse():
     return ap.parse_args()
 
 
-# rocprofv3 kernel names of each call kind (substring of the demangled name)
+# rocprofv3 kernel names of each call kind (regular expressions on the
+# demangled name; template arguments: addressing, dtype, first micro-step)
 KERNEL_NAMES = {
-    "accumulate_first": "k_accumulate_all<2, true>",
-    "accumulate": "k_accumulate_all<2, false>",
-    "accumulate_reduce": "k_reduce<",
-    "adamw": "k_adamw<",
+    "accumulate_first": r"k_accumulate_all<\w+, \d, true>",
+    "accumulate": r"k_accumulate_all<\w+, \d, false>",
+    "accumulate_reduce": r"k_reduce<",
+    "adamw": r"k_adamw<",
 }
 COPY_KERNEL = "copyBuffer"  # the runtime's plain device-to-device copy
 
@@ -70,26 +72,25 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calib_byte
     import csv
 
     def load(path, counter):
-        rows = {}
-        for r in csv.DictReader(open(path)):
+        rows, first_copy = {}, None
+        for r in sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"])):
             if r.get("Counter_Name", counter) != counter:
                 continue
             name = r.get("Kernel_Name", "")
             rows.setdefault(name, []).append(float(r["Counter_Value"]))
-        return rows
+            if first_copy is None and COPY_KERNEL in name:
+                first_copy = float(r["Counter_Value"])  # the calibration copies run first
+        return rows, first_copy
 
-    fetch = load(fetch_csv, "FETCH_SIZE")
-    write = load(write_csv, "WRITE_SIZE")
+    fetch, f_kib = load(fetch_csv, "FETCH_SIZE")
+    write, w_kib = load(write_csv, "WRITE_SIZE")
+
+    import re
 
     def per_kind(rows, key):
-        vals = [v for name, vs in rows.items() if key in name for v in vs]
+        vals = [v for name, vs in rows.items() if re.search(key, name) for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    copy_f = [v for name, vs in fetch.items() if COPY_KERNEL in name and "dpk" not in name for v in vs]
-    copy_w = [v for name, vs in write.items() if COPY_KERNEL in name and "dpk" not in name for v in vs]
-    # the copies of calib_bytes are the largest copy dispatches
-    f_kib = sorted(copy_f)[-1]
-    w_kib = sorted(copy_w)[-1]
     f_fac = calib_bytes / (f_kib * 1024.0)
     w_fac = calib_bytes / (w_kib * 1024.0)
     out = {}
@@ -104,8 +105,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calib_byte
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def bytes_model(w) -> dict:

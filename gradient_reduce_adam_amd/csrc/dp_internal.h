@@ -12,7 +12,9 @@ namespace dpk {
 constexpr int kWave = 64;                 // threads per streaming workgroup: one wave64
 constexpr int kPiece = 4 * kWave;         // elements per streaming workgroup: 4 per lane
 constexpr int kFoldThreads = 256;         // threads of the statistics fold workgroups
-constexpr int64_t kMaxBlocksPerLaunch = int64_t{1} << 24;  // keeps gridDim.x * kWave below 2^32
+// workgroups per dispatch: gridDim.x * kWave must stay below 2^32, so one call
+// covers up to 2^26 pieces (17e9 elements) in a single dispatch
+constexpr int64_t kMaxBlocksPerLaunch = (int64_t{1} << 26) - 1;
 
 // The pieces of one call's range [begin, end), as the kernels see them.
 //  flat:  every role of the call is one flat buffer; piece p covers flat
