@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
     ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
                     help="bind the state as flat buffers, or through per-tensor pointer tables (same memory)")
+    ap.add_argument("--update", choices=("auto", "two-pass", "single-pass"), default="auto",
+                    help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
+                         "update in one read of the state (runs without clipping); auto: single-pass when the "
+                         "workload does not clip")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -60,6 +64,7 @@ KERNEL_NAMES = {
     "accumulate": r"k_accumulate_all<\w+, \d, false>",
     "accumulate_reduce": r"k_reduce<",
     "adamw": r"k_adamw<",
+    "reduce_adamw": r"k_reduce_adamw<",
 }
 COPY_KERNEL = "copyBuffer"  # the runtime's plain device-to-device copy
 
@@ -112,10 +117,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def bytes_model(w) -> dict:
+def single_pass_for(w, update: str) -> bool:
+    if update == "single-pass" and w.max_norm > 0.0:
+        raise SystemExit(f"{w.name} clips at {w.max_norm}: the single pass needs the norm before the update")
+    return update == "single-pass" or (update == "auto" and w.max_norm == 0.0)
+
+
+def bytes_model(w, single: bool = False) -> dict:
     """Algorithmic HBM bytes per parameter of each call kind in one step of
-    the fused sequence: micro-steps 1 .. a-1 of every replica per launch, the
-    last micro-step fused with the replica average, then the update."""
+    the fused sequence: micro-steps 1 .. a-1 of every replica per launch, then
+    either the last micro-step fused with the replica average followed by the
+    update (two passes: g_bar is written and read back), or the last
+    micro-step, the average and the update in one pass (g_bar never stored)."""
     sg, sp = 2.0, 2.0
     per = {}
     last = 1 if w.partials else w.a
@@ -123,19 +136,38 @@ def bytes_model(w) -> dict:
         per["accumulate_first"] = w.n * (sg + 4.0)
     if last >= 3:
         per["accumulate"] = w.n * (last - 2) * (sg + 8.0)
-    per["accumulate_reduce"] = w.n * (sg + (4.0 if last >= 2 else 0.0)) + 4.0
-    per["adamw"] = 16.0 + 12.0 + sp
+    sources = w.n * (sg + (4.0 if last >= 2 else 0.0))
+    if single:
+        per["reduce_adamw"] = sources + 12.0 + 12.0 + sp
+    else:
+        per["accumulate_reduce"] = sources + 4.0
+        per["adamw"] = 16.0 + 12.0 + sp
     return per
 
 
-def launch_bytes(w, kind: str) -> float:
+def unfused_bytes_per_param(w) -> float:
+    """Compulsory bytes per parameter of the step done as separate passes:
+    every micro-step a read-modify-write of its accumulator, the replica
+    average reading the accumulators and writing g_bar, the update reading
+    g_bar once (with n = 1, g_bar is the accumulator; incoming partials are
+    read once).  The step time against these bytes is the bandwidth an
+    unfused implementation would need to match it."""
+    sg = 2.0
+    if w.partials:
+        return w.n * sg + 4.0 + 30.0
+    if w.n == 1:
+        return w.a * (sg + 8.0) + 26.0
+    return w.n * w.a * (sg + 8.0) + 4.0 + 30.0
+
+
+def launch_bytes(w, kind: str, single: bool = False) -> float:
     """Algorithmic bytes of one launch of `kind` over the whole flat space."""
-    per = bytes_model(w)
+    per = bytes_model(w, single)
     launches = {"accumulate": max(1, (1 if w.partials else w.a) - 2)}
     return w.P * per[kind] / launches.get(kind, 1)
 
 
-def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat"):
+def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False):
     import torch
 
     import synth
@@ -152,7 +184,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
-                      growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk)
+                      growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -163,12 +195,13 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         def per_tensor(t):
             return [t.data_ptr() + o * t.element_size() for o in off]
 
-        for role, t in (("master", d.master), ("exp_avg", d.exp_avg), ("exp_avg_sq", d.exp_avg_sq),
-                        ("param", d.param)):
-            d.plan.bind_tensors(role, per_tensor(t))
+        for b, (w_, m_, v_) in enumerate(d.banks):
+            for role, t in (("master", w_), ("exp_avg", m_), ("exp_avg_sq", v_)):
+                d.plan.bind_tensors(role, per_tensor(t), b)
+        d.plan.bind_tensors("param", per_tensor(d.param))
         for r, t in enumerate(d.acc):
             d.plan.bind_tensors("acc", per_tensor(t), r)
-        if not (w.n == 1 and not w.partials):
+        if d.gbar is not None and not (w.n == 1 and not w.partials):
             d.plan.bind_tensors("gbar", per_tensor(d.gbar))
 
     # one batch of gradients, resident before the timed region
@@ -176,7 +209,9 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     per_buf = 2 * w.P
     # a ring of distinct buffers; a micro-step's n replicas (and consecutive
     # launches) never share one, and every buffer is far larger than the caches
-    nbuf = len(calls) if len(calls) * per_buf <= RESIDENT_GRAD_BUDGET else int(RESIDENT_GRAD_BUDGET // per_buf)
+    free, _ = torch.cuda.mem_get_info()
+    budget = min(RESIDENT_GRAD_BUDGET, free - 4e9)  # leave room for the library's tables and torch
+    nbuf = len(calls) if len(calls) * per_buf <= budget else int(budget // per_buf)
     nbuf = max(nbuf, 2 * w.n if not w.partials else w.n)
     bufs = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(nbuf)]
     addr = {}
@@ -211,6 +246,9 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
                   lambda k=k: plan.accumulate_all(first=(k == 1), stream=stream), rec)
         for r in range(w.n):
             dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, last)])
+        if single:  # one call: the single-pass kernel, the statistics fold and the (idle) parameter restore
+            timed("reduce_adamw", lambda: plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
+            return
         timed("accumulate_reduce", lambda: plan.accumulate_reduce(stream=stream), rec)
         timed("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream), rec)
         timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
@@ -281,15 +319,17 @@ def main():
         print(json.dumps(res, indent=1))
         return
     w = workloads.by_name(args.workload)
-    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration, args.bind)
+    single = single_pass_for(w, args.update)
+    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration, args.bind,
+                                       single)
     ms_per_step = elapsed * 1e3 / args.steps
-    per_param = bytes_model(w)
+    per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: the call kind that moves the most algorithmic bytes per step
     dom = max(per_param, key=lambda k: per_param[k])
-    dom_bytes = launch_bytes(w, dom)
+    dom_bytes = launch_bytes(w, dom, single)
     dom_ms = per_kind[dom]["avg_ms"]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = None
@@ -317,10 +357,13 @@ def main():
                    "grad_dtype": w.grad_dtype, "param_dtype": w.param_dtype, "state": "fp32 master/m/v",
                    "update_arithmetic": "f64", "clip": w.max_norm, "loss_scale": w.scaler,
                    "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)",
-                   "chunk_elems": args.chunk or 16384, "binding": args.bind},
+                   "chunk_elems": args.chunk or 16384, "binding": args.bind,
+                   "update": "single-pass" if single else "two-pass"},
         "hbm_gbps": hbm_gbps,
         "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
         "bytes_per_param_step": sum(per_param.values()),
+        "unfused_bytes_per_param_step": unfused_bytes_per_param(w),
+        "unfused_equiv_gbps": unfused_bytes_per_param(w) * w.P / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "bytes_per_launch": dom_bytes,
                      "avg_launch_ms": dom_ms},

@@ -39,7 +39,7 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
-           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_read_state")
+           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state")
 
 
 class Layout(ctypes.Structure):
@@ -61,7 +61,7 @@ class AdamHparams(ctypes.Structure):
 class StepState(ctypes.Structure):
     _fields_ = [("t", ctypes.c_int64), ("iter", ctypes.c_int64), ("growth_tracker", ctypes.c_int64),
                 ("beta1_pow", ctypes.c_double), ("beta2_pow", ctypes.c_double), ("scale", ctypes.c_double),
-                ("found_inf", ctypes.c_int32), ("reserved", ctypes.c_int32), ("sumsq", ctypes.c_double),
+                ("found_inf", ctypes.c_int32), ("bank", ctypes.c_int32), ("sumsq", ctypes.c_double),
                 ("norm", ctypes.c_double), ("clip", ctypes.c_double), ("gscale", ctypes.c_double)]
 
     def as_dict(self) -> dict:
@@ -75,7 +75,8 @@ class PlanInfo(ctypes.Structure):
                 ("bytes_accumulate", ctypes.c_double), ("bytes_reduce_acc", ctypes.c_double),
                 ("bytes_reduce_partials", ctypes.c_double), ("bytes_accumulate_reduce", ctypes.c_double),
                 ("bytes_stats_scan", ctypes.c_double),
-                ("bytes_adam", ctypes.c_double)]
+                ("bytes_adam", ctypes.c_double), ("bytes_reduce_adam", ctypes.c_double),
+                ("bytes_reduce_adam_partials", ctypes.c_double)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
@@ -145,6 +146,7 @@ def _load():
         "dp_reduce_replicas": (ctypes.c_int, [vp, ctypes.c_int, vp]),
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
+        "dp_reduce_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), vp]),
         "dp_read_state": (ctypes.c_int, [vp, ctypes.POINTER(StepState), vp]),
     }
     for name, (res, args) in sig.items():
@@ -272,6 +274,11 @@ def dp_adam_step(plan: int, lr: float, eps: float, weight_decay: float, shard_be
                             ctypes.c_void_p(_stream(stream))))
 
 
+def dp_reduce_adam_step(plan: int, lr: float, eps: float, weight_decay: float, stream=None) -> None:
+    hp = AdamHparams(lr, eps, weight_decay)
+    _check(lib.dp_reduce_adam_step(ctypes.c_void_p(plan), ctypes.byref(hp), ctypes.c_void_p(_stream(stream))))
+
+
 def dp_read_state(plan: int, stream=None) -> dict:
     st = StepState()
     _check(lib.dp_read_state(ctypes.c_void_p(plan), ctypes.byref(st), ctypes.c_void_p(_stream(stream))))
@@ -346,6 +353,9 @@ class Plan:
     def adam_step(self, lr: float, eps: float, weight_decay: float, begin: int = 0, end: Optional[int] = None,
                   stream=None) -> None:
         dp_adam_step(self.handle, lr, eps, weight_decay, begin, self.P if end is None else end, stream)
+
+    def reduce_adam_step(self, lr: float, eps: float, weight_decay: float, stream=None) -> None:
+        dp_reduce_adam_step(self.handle, lr, eps, weight_decay, stream)
 
     def read_state(self, stream=None) -> dict:
         return dp_read_state(self.handle, stream)

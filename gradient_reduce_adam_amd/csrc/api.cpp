@@ -96,6 +96,17 @@ struct dp_plan {
 
 namespace {
 
+// Both banks of the optimizer state (bank 1 null when unbound).
+dpk::StateRefs state_refs(const dp_plan* p) {
+    dpk::StateRefs s{};
+    for (int b = 0; b < 2; ++b) {
+        s.w[b] = p->roles[DP_ROLE_MASTER][b].ref();
+        s.m[b] = p->roles[DP_ROLE_EXP_AVG][b].ref();
+        s.v[b] = p->roles[DP_ROLE_EXP_AVG_SQ][b].ref();
+    }
+    return s;
+}
+
 // Chunk table of [begin, end): every tensor piece inside the range, split at
 // multiples of chunk_elems counted from the tensor's start (so a chunk keeps
 // the tensor's alignment), in flat order.
@@ -177,6 +188,7 @@ dp_status range_table(dp_plan* p, int64_t begin, int64_t end, const DeviceTable*
 
 bool role_ok(dp_role r) { return r >= DP_ROLE_PARAM && r <= DP_ROLE_GBAR; }
 bool per_replica(dp_role r) { return r == DP_ROLE_GRAD || r == DP_ROLE_ACC; }
+bool banked(dp_role r) { return r == DP_ROLE_MASTER || r == DP_ROLE_EXP_AVG || r == DP_ROLE_EXP_AVG_SQ; }
 
 const Binding* gbar_binding(const dp_plan* p) {
     const Binding* b = &p->roles[DP_ROLE_GBAR][0];
@@ -200,6 +212,12 @@ bool all_flat(std::initializer_list<dpk::RoleRef> refs) {
 bool all_flat(const dpk::Srcs& s, int n) {
     for (int i = 0; i < n; ++i)
         if (s.r[i].tab) return false;
+    return true;
+}
+
+bool all_flat(const dpk::StateRefs& s) {
+    for (int b = 0; b < 2; ++b)
+        if (s.w[b].tab || s.m[b].tab || s.v[b].tab) return false;
     return true;
 }
 
@@ -305,6 +323,8 @@ dp_status dp_plan_info_get(const dp_plan* p, dp_plan_info* out) {
     out->bytes_accumulate_reduce = P * ((sg + 4.0) * p->n + 4.0);
     out->bytes_stats_scan = P * 4.0;
     out->bytes_adam = P * (16.0 + 12.0 + sp);
+    out->bytes_reduce_adam = P * ((sg + 4.0) * p->n + 12.0 + 12.0 + sp);
+    out->bytes_reduce_adam_partials = P * (sg * p->n + 12.0 + 12.0 + sp);
     return DP_OK;
 }
 
@@ -325,7 +345,7 @@ dp_status dp_plan_chunks(const dp_plan* p, int64_t begin, int64_t end, int64_t f
 static dp_status bind_check(dp_plan* p, dp_role role, int32_t replica) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "bind: null plan");
     if (!role_ok(role)) return fail(DP_ERR_INVALID_ARG, "bind: unknown role %d", static_cast<int>(role));
-    const int32_t lim = per_replica(role) ? p->n : 1;
+    const int32_t lim = per_replica(role) ? p->n : (banked(role) ? 2 : 1);
     if (replica < 0 || replica >= lim)
         return fail(DP_ERR_INVALID_ARG, "bind: replica %d outside [0, %d) for role %d", replica, lim, static_cast<int>(role));
     return DP_OK;
@@ -396,12 +416,16 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     if (!p->state) {
         hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->state), sizeof(dpk::DevState));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of the state block: %s", hipGetErrorString(e));
-        const size_t np = static_cast<size_t>(
-            std::max<int64_t>(std::max(p->full.npieces(true), p->full.npieces(false)), 1));
+        // statistics are always written on table pieces of [0, P): one slot
+        // per piece, grouped by XCD; the slots no piece maps to stay zero
+        const size_t np = static_cast<size_t>(dpk::stats_slots(std::max<int64_t>(p->full.npieces(false), 1)));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.sumsq), np * sizeof(double));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
         e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
+        e = hipMemset(p->stats.sumsq, 0, np * sizeof(double));
+        if (e == hipSuccess) e = hipMemset(p->stats.bad, 0, np * sizeof(uint32_t));
+        if (e != hipSuccess) return hip_fail(e, "hipMemset of statistics partials");
         const size_t ng = (np + dpk::kFoldGroup - 1) / dpk::kFoldGroup;
         e = hipMalloc(reinterpret_cast<void**>(&p->fold.sumsq), ng * sizeof(double));
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics groups: %s", hipGetErrorString(e));
@@ -574,7 +598,7 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
         return fail(DP_ERR_STATE, "no fused statistics for the current g_bar: reduce first, or pass scan = 1");
     }
     dpk::ScalerArgs a{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, max_norm,
-                      p->cfg.scaler_mode, p->cfg.growth_interval};
+                      p->cfg.scaler_mode, p->cfg.growth_interval, 0};
     const int64_t nparts = p->full.count > 0 ? p->partials_count : 0;
     s = check_launch(dpk::launch_finalize(p->stats, nparts, p->fold, p->state, a, stream), "finalize launch");
     if (s != DP_OK) return s;
@@ -604,11 +628,63 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
     s = range_table(p, begin, end, &t);
     if (s != DP_OK) return s;
     dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
-    const dpk::RoleRef w = p->roles[DP_ROLE_MASTER][0].ref(), m = p->roles[DP_ROLE_EXP_AVG][0].ref(),
-                       v = p->roles[DP_ROLE_EXP_AVG_SQ][0].ref(), pr = p->roles[DP_ROLE_PARAM][0].ref();
-    return check_launch(dpk::launch_adamw(p->pdt, t->table(all_flat({gb->ref(), w, m, v, pr})), gb->ref(), w, m, v, pr,
-                                          p->state, a, stream),
+    const dpk::StateRefs sr = state_refs(p);
+    const dpk::RoleRef pr = p->roles[DP_ROLE_PARAM][0].ref();
+    const bool flat = all_flat(sr) && all_flat({gb->ref(), pr});
+    return check_launch(dpk::launch_adamw(p->pdt, t->table(flat), gb->ref(), sr, pr, p->state, a, stream),
                         "adamw launch");
+}
+
+dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t stream) {
+    if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_step: null argument");
+    if (!(hp->lr >= 0.0) || !(hp->eps > 0.0) || !(hp->weight_decay >= 0.0))
+        return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_step before dp_state_init");
+    dpk::Srcs grads{}, accs{};
+    dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+    if (s != DP_OK) return s;
+    for (int32_t r = 0; r < p->n; ++r)
+        if (p->micro[r] != p->micro[0])
+            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
+                        p->micro[r], p->micro[0]);
+    const bool with_acc = p->micro[0] > 0;
+    if (with_acc) {
+        s = bound_replicas(p, DP_ROLE_ACC, &accs);
+        if (s != DP_OK) return s;
+    }
+    static const char* const names[] = {"MASTER", "EXP_AVG", "EXP_AVG_SQ"};
+    for (int role = DP_ROLE_MASTER; role <= DP_ROLE_EXP_AVG_SQ; ++role)
+        for (int b = 0; b < 2; ++b)
+            if (!p->roles[role][b].bound)
+                return fail(DP_ERR_UNBOUND, "role %s bank %d is not bound (the single pass writes the other bank)",
+                            names[role - DP_ROLE_MASTER], b);
+    s = need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
+    if (s != DP_OK) return s;
+    s = ensure_full(p);
+    if (s != DP_OK) return s;
+    const dpk::StateRefs sr = state_refs(p);
+    const dpk::RoleRef pr = p->roles[DP_ROLE_PARAM][0].ref();
+    const dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
+    const dpk::Table t = p->full.table(false);  // statistics: table pieces
+    if (t.npieces > 0) {
+        s = check_launch(dpk::launch_reduce_adamw(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
+                                                  p->gdt, p->pdt, p->n, t, accs, grads, sr, pr, p->stats, p->state, a,
+                                                  stream),
+                         "reduce + adamw launch");
+        if (s != DP_OK) return s;
+    }
+    const dpk::ScalerArgs sc{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, 0.0,
+                             p->cfg.scaler_mode, p->cfg.growth_interval, 1};
+    s = check_launch(dpk::launch_finalize(p->stats, t.npieces, p->fold, p->state, sc, stream), "finalize launch");
+    if (s != DP_OK) return s;
+    s = check_launch(dpk::launch_restore_param(p->pdt, p->full.table(all_flat(sr) && all_flat({pr})), sr, pr, p->state,
+                                               stream),
+                     "parameter restore launch");
+    if (s != DP_OK) return s;
+    std::fill(p->micro.begin(), p->micro.end(), 0);
+    p->partials_valid = false;
+    p->stats_current = false;
+    return DP_OK;
 }
 
 dp_status dp_read_state(dp_plan* p, dp_step_state* out, hipStream_t stream) {

@@ -46,17 +46,22 @@ struct Srcs {
 struct DevState {
     int64_t t, iter, growth_tracker;
     double beta1_pow, beta2_pow, scale;
-    int32_t found_inf, reserved;
+    int32_t found_inf, bank;
     double sumsq, norm, clip, gscale;
 };
 static_assert(sizeof(DevState) == sizeof(dp_step_state), "DevState must mirror dp_step_state");
 
 // Per-piece statistics of g_bar: binary64 sum of squares and the count of
-// non-finite entries.  Index = position of the piece in the [0, P) table.
+// non-finite entries of piece p of the [0, P) table, at slot
+// (p % 8) * ceil(npieces / 8) + p / 8.  Consecutive workgroups go round-robin
+// to the 8 XCDs, so this keeps the slots one XCD writes contiguous in its own
+// L2 and they leave it as whole lines.  The fold adds the slots in slot order;
+// the few slots no piece maps to stay zero.
 struct StatsBuf {
     double* sumsq;
     uint32_t* bad;
 };
+inline int64_t stats_slots(int64_t npieces) { return 8 * ((npieces + 7) / 8); }
 
 // Second level of the statistics fold: one entry per group of kFoldGroup
 // piece partials (used when a table has more than kFoldGroup pieces).
@@ -73,6 +78,15 @@ struct AdamArgs {
 struct ScalerArgs {
     double beta1, beta2, backoff, growth, max_norm;
     int32_t mode, growth_interval;
+    int32_t flip_bank;  // an applied step makes the other state bank current
+};
+
+// The optimizer state in two banks: bank st->bank is current.  The two-pass
+// update works in place on the current bank; the single-pass update reads it
+// and writes the other one.  Bank 1 is unbound (null) unless the caller gave
+// one.
+struct StateRefs {
+    RoleRef w[2], m[2], v[2];
 };
 
 hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
@@ -91,8 +105,18 @@ hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, c
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t stream);
-hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& s, RoleRef p,
                         const DevState* st, const AdamArgs& args, hipStream_t stream);
+// Single pass: the replica average of launch_reduce (same sources, order and
+// statistics) feeding the update of every element, from the current bank into
+// the other, with the scalars the step will have if it is applied (no clip).
+hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, const Srcs& accs,
+                               const Srcs& grads, const StateRefs& s, RoleRef p, StatsBuf sb, const DevState* st,
+                               const AdamArgs& args, hipStream_t stream);
+// After a skipped single-pass step: p = RNE(w) from the current bank again
+// (does nothing when the step was applied).
+hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& s, RoleRef p, const DevState* st,
+                                hipStream_t stream);
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t stream);
 
 }  // namespace dpk

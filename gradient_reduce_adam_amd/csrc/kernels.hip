@@ -150,16 +150,18 @@ __device__ __forceinline__ void add_stats(float y, double& ss, uint32_t& bad) {
     bad += nonfinite(y);
 }
 
-// Fixed-order wave64 butterfly of (sumsq, bad); lane 0 writes partial p.
-__device__ __forceinline__ void wave_stats_store(double ss, uint32_t bad, int64_t p, StatsBuf sb) {
+// Fixed-order wave64 butterfly of (sumsq, bad); lane 0 writes the partial of
+// piece p (of npieces) to its XCD-grouped slot.
+__device__ __forceinline__ void wave_stats_store(double ss, uint32_t bad, int64_t p, int64_t npieces, StatsBuf sb) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         ss += __shfl_xor(ss, off, 64);
         bad += __shfl_xor(bad, off, 64);
     }
     if (threadIdx.x == 0) {
-        sb.sumsq[p] = ss;
-        sb.bad[p] = bad;
+        const int64_t slot = (p & 7) * ((npieces + 7) >> 3) + (p >> 3);
+        sb.sumsq[slot] = ss;
+        sb.bad[slot] = bad;
     }
 }
 
@@ -229,7 +231,7 @@ __global__ void __launch_bounds__(kWave) k_accumulate(Table t, int64_t base, Rol
     double ss = 0.0;
     uint32_t bad = 0;
     accumulate_piece<kGrad, kFirst, kStats>(q, grad, acc, ss, bad);
-    if constexpr (kStats) wave_stats_store(ss, bad, p, sb);
+    if constexpr (kStats) wave_stats_store(ss, bad, p, t.npieces, sb);
 }
 
 // every replica's micro-step in one launch: blockIdx.y is the replica (the
@@ -249,32 +251,29 @@ __global__ void __launch_bounds__(kWave) k_accumulate_all(Table t, int64_t base,
 //   kMode 2: x_r = acc_r + g_r           (the last micro-step fused: acc_r is
 //                                         not written back)
 // ============================================================================
-template <bool kFlat, int kMode, int kGrad, int N>
-__global__ void __launch_bounds__(kWave) k_reduce(Table t, int64_t base, Srcs accs, Srcs grads, RoleRef gbar,
-                                                    StatsBuf sb) {
-    const int64_t p = base + blockIdx.x;
-    const Piece q = piece_of<kFlat>(t, p);
+template <int kMode, int kGrad, int N>
+struct ReduceSrc {
     const float* ap[N];
     const uint16_t* gp[N];
-    bool ok = true;
+    bool ok;  // every source pointer of the piece allows the vector path
+
+    __device__ __forceinline__ ReduceSrc(const Piece& q, const Srcs& accs, const Srcs& grads) {
+        ok = true;
 #pragma unroll
-    for (int r = 0; r < N; ++r) {
-        if constexpr (kMode != 1) {
-            ap[r] = elem_ptr<const float>(accs.r[r], q);
-            ok = ok && aligned(ap[r], 16);
-        }
-        if constexpr (kMode != 0) {
-            gp[r] = elem_ptr<const uint16_t>(grads.r[r], q);
-            ok = ok && aligned(gp[r], 8);
+        for (int r = 0; r < N; ++r) {
+            if constexpr (kMode != 1) {
+                ap[r] = elem_ptr<const float>(accs.r[r], q);
+                ok = ok && aligned(ap[r], 16);
+            }
+            if constexpr (kMode != 0) {
+                gp[r] = elem_ptr<const uint16_t>(grads.r[r], q);
+                ok = ok && aligned(gp[r], 8);
+            }
         }
     }
-    float* __restrict__ out = elem_ptr<float>(gbar, q);
-    ok = ok && aligned(out, 16);
-    const int lane = threadIdx.x;
-    const LaneSpan l = lane_span(q);
-    double ss = 0.0;
-    uint32_t bad = 0;
-    if (l.full && ok) {
+
+    // the average of this lane's 4 elements (vector path)
+    __device__ __forceinline__ f32x4 vec(int lane) const {
         float x[4][N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
@@ -287,26 +286,46 @@ __global__ void __launch_bounds__(kWave) k_reduce(Table t, int64_t base, Srcs ac
         }
         f32x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            y[e] = average<N>(tree_sum<N>(x[e]));
-            add_stats(y[e], ss, bad);
+        for (int e = 0; e < 4; ++e) y[e] = average<N>(tree_sum<N>(x[e]));
+        return y;
+    }
+
+    // the average of element i (per-element path)
+    __device__ __forceinline__ float elem(int i) const {
+        float x[N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            if constexpr (kMode == 0) x[r] = ldg<float>(ap[r], i);
+            else if constexpr (kMode == 1) x[r] = widen1<kGrad>(ldg<uint16_t>(gp[r], i));
+            else x[r] = ldg<float>(ap[r], i) + widen1<kGrad>(ldg<uint16_t>(gp[r], i));
         }
-        stg_nt<f32x4>(out, lane, y);
+        return average<N>(tree_sum<N>(x));
+    }
+};
+
+template <bool kFlat, int kMode, int kGrad, int N>
+__global__ void __launch_bounds__(kWave) k_reduce(Table t, int64_t base, Srcs accs, Srcs grads, RoleRef gbar,
+                                                    StatsBuf sb) {
+    const int64_t p = base + blockIdx.x;
+    const Piece q = piece_of<kFlat>(t, p);
+    const ReduceSrc<kMode, kGrad, N> src(q, accs, grads);
+    float* __restrict__ out = elem_ptr<float>(gbar, q);
+    const LaneSpan l = lane_span(q);
+    double ss = 0.0;
+    uint32_t bad = 0;
+    if (l.full && src.ok && aligned(out, 16)) {
+        const f32x4 y = src.vec(threadIdx.x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) add_stats(y[e], ss, bad);
+        stg_nt<f32x4>(out, threadIdx.x, y);
     } else {
         for (int i = l.lo; i < l.hi; ++i) {
-            float x[N];
-#pragma unroll
-            for (int r = 0; r < N; ++r) {
-                if constexpr (kMode == 0) x[r] = ldg<float>(ap[r], i);
-                else if constexpr (kMode == 1) x[r] = widen1<kGrad>(ldg<uint16_t>(gp[r], i));
-                else x[r] = ldg<float>(ap[r], i) + widen1<kGrad>(ldg<uint16_t>(gp[r], i));
-            }
-            const float y = average<N>(tree_sum<N>(x));
+            const float y = src.elem(i);
             stg<float>(out, i, y);
             add_stats(y, ss, bad);
         }
     }
-    wave_stats_store(ss, bad, p, sb);
+    wave_stats_store(ss, bad, p, t.npieces, sb);
 }
 
 // ============================================================================
@@ -327,11 +346,11 @@ __global__ void __launch_bounds__(kWave) k_stats(Table t, int64_t base, RoleRef 
     } else {
         for (int i = l.lo; i < l.hi; ++i) add_stats(ldg<float>(x, i), ss, bad);
     }
-    wave_stats_store(ss, bad, p, sb);
+    wave_stats_store(ss, bad, p, t.npieces, sb);
 }
 
 // ============================================================================
-// pass 2: the piece partials are folded in a fixed order -- by groups of
+// pass 2: the statistics slots are folded in slot order -- by groups of
 // kFoldGroup when there are many -- and one workgroup updates the scalar state
 // ============================================================================
 template <typename Count>
@@ -360,9 +379,9 @@ __device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, con
     bad_out = s_bad[0];
 }
 
-__global__ void __launch_bounds__(kFoldThreads) k_fold(StatsBuf sb, int64_t nparts, FoldBuf fold) {
+__global__ void __launch_bounds__(kFoldThreads) k_fold(StatsBuf sb, int64_t nslots, FoldBuf fold) {
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFoldGroup;
-    const int64_t hi = lo + kFoldGroup < nparts ? lo + kFoldGroup : nparts;
+    const int64_t hi = lo + kFoldGroup < nslots ? lo + kFoldGroup : nslots;
     double ss;
     uint64_t bad;
     block_fold(sb.sumsq, sb.bad, lo, hi, ss, bad);
@@ -374,11 +393,11 @@ __global__ void __launch_bounds__(kFoldThreads) k_fold(StatsBuf sb, int64_t npar
 
 template <typename Count>
 __global__ void __launch_bounds__(kFoldThreads) k_finalize(const double* __restrict__ ss_in,
-                                                             const Count* __restrict__ bad_in, int64_t nparts,
+                                                             const Count* __restrict__ bad_in, int64_t nslots,
                                                              DevState* __restrict__ st, ScalerArgs args) {
     double sumsq;
     uint64_t badsum;
-    block_fold(ss_in, bad_in, 0, nparts, sumsq, badsum);
+    block_fold(ss_in, bad_in, 0, nslots, sumsq, badsum);
     if (threadIdx.x != 0) return;
     DevState s = *st;
     s.sumsq = sumsq;
@@ -397,6 +416,7 @@ __global__ void __launch_bounds__(kFoldThreads) k_finalize(const double* __restr
         s.t += 1;
         s.beta1_pow *= args.beta1;
         s.beta2_pow *= args.beta2;
+        if (args.flip_bank) s.bank ^= 1;
         if (args.mode == DP_SCALER_DYNAMIC) {
             s.growth_tracker += 1;
             if (s.growth_tracker == args.growth_interval) {
@@ -419,7 +439,7 @@ __global__ void k_state_init(DevState* __restrict__ st, double scale) {
     s.beta2_pow = 1.0;
     s.scale = scale;
     s.found_inf = 0;
-    s.reserved = 0;
+    s.bank = 0;
     s.sumsq = 0.0;
     s.norm = 0.0;
     s.clip = 1.0;
@@ -434,6 +454,23 @@ __global__ void k_state_init(DevState* __restrict__ st, double scale) {
 struct AdamCoef {
     double gscale, b1, omb1, b2, omb2, step, sqrt_bc2, eps, dec;
 };
+
+// The coefficients of the update with gradient factor gscale and bias
+// corrections 1 - b1p, 1 - b2p (b1p = beta1^t, b2p = beta2^t of the step).
+__device__ __forceinline__ AdamCoef adam_coef(double gscale, double b1p, double b2p, const AdamArgs& args) {
+#pragma clang fp contract(off)
+    AdamCoef k;
+    k.gscale = gscale;
+    k.b1 = args.beta1;
+    k.omb1 = 1.0 - args.beta1;
+    k.b2 = args.beta2;
+    k.omb2 = 1.0 - args.beta2;
+    k.step = args.lr / (1.0 - b1p);
+    k.sqrt_bc2 = sqrt(1.0 - b2p);
+    k.eps = args.eps;
+    k.dec = 1.0 - args.lr * args.weight_decay;
+    return k;
+}
 
 // One element of the update.  Every operation is a separately rounded IEEE
 // binary64 operation in the order written (no contraction into fused
@@ -451,58 +488,144 @@ __device__ __forceinline__ void adam1(float gb, float& w, float& m, float& v, co
     w = static_cast<float>(wi);
 }
 
-template <bool kFlat, int kParam>
-__global__ void __launch_bounds__(kWave) k_adamw(Table t, int64_t base, RoleRef gbar, RoleRef wr, RoleRef mr,
-                                                   RoleRef vr, RoleRef pr, const DevState* __restrict__ st,
-                                                   AdamArgs args) {
-    if (st->found_inf) return;
-    AdamCoef k;
-    {
-#pragma clang fp contract(off)
-        k.gscale = st->gscale;
-        k.b1 = args.beta1;
-        k.omb1 = 1.0 - args.beta1;
-        k.b2 = args.beta2;
-        k.omb2 = 1.0 - args.beta2;
-        k.step = args.lr / (1.0 - st->beta1_pow);
-        k.sqrt_bc2 = sqrt(1.0 - st->beta2_pow);
-        k.eps = args.eps;
-        k.dec = 1.0 - args.lr * args.weight_decay;
+template <int kParam>
+__device__ __forceinline__ u32x2 narrow4(const float (&w)[4]) {
+    return u32x2{static_cast<uint32_t>(narrow1<kParam>(w[0])) | (static_cast<uint32_t>(narrow1<kParam>(w[1])) << 16),
+                 static_cast<uint32_t>(narrow1<kParam>(w[2])) | (static_cast<uint32_t>(narrow1<kParam>(w[3])) << 16)};
+}
+
+// The state of one piece: read from bank rd, written to bank wr (the same
+// bank for the in-place update).
+struct StatePtrs {
+    const float* w_in;
+    const float* m_in;
+    const float* v_in;
+    float* w_out;
+    float* m_out;
+    float* v_out;
+    uint16_t* p;
+    bool ok;  // the vector path is allowed
+
+    __device__ __forceinline__ StatePtrs(const StateRefs& s, RoleRef pr, int rd, int wr, const Piece& q) {
+        w_in = elem_ptr<const float>(s.w[rd], q);
+        m_in = elem_ptr<const float>(s.m[rd], q);
+        v_in = elem_ptr<const float>(s.v[rd], q);
+        w_out = elem_ptr<float>(s.w[wr], q);
+        m_out = elem_ptr<float>(s.m[wr], q);
+        v_out = elem_ptr<float>(s.v[wr], q);
+        p = elem_ptr<uint16_t>(pr, q);
+        ok = aligned(w_in, 16) && aligned(m_in, 16) && aligned(v_in, 16) && aligned(w_out, 16) &&
+             aligned(m_out, 16) && aligned(v_out, 16) && aligned(p, 8);
     }
-    const Piece q = piece_of<kFlat>(t, base + blockIdx.x);
-    const float* __restrict__ gp = elem_ptr<const float>(gbar, q);
-    float* __restrict__ wp = elem_ptr<float>(wr, q);
-    float* __restrict__ mp = elem_ptr<float>(mr, q);
-    float* __restrict__ vp = elem_ptr<float>(vr, q);
-    uint16_t* __restrict__ pp = elem_ptr<uint16_t>(pr, q);
-    const int lane = threadIdx.x;
-    const LaneSpan l = lane_span(q);
-    if (l.full && aligned(gp, 16) && aligned(wp, 16) && aligned(mp, 16) && aligned(vp, 16) && aligned(pp, 8)) {
-        const f32x4 G = ldg_nt<f32x4>(gp, lane);
-        const f32x4 W = ldg_nt<f32x4>(wp, lane);
-        const f32x4 M = ldg_nt<f32x4>(mp, lane);
-        const f32x4 V = ldg_nt<f32x4>(vp, lane);
+
+    // this lane's 4 elements with gradient G (vector path)
+    template <int kParam>
+    __device__ __forceinline__ void update4(f32x4 G, int lane, const AdamCoef& k) const {
+        const f32x4 W = ldg_nt<f32x4>(w_in, lane);
+        const f32x4 M = ldg_nt<f32x4>(m_in, lane);
+        const f32x4 V = ldg_nt<f32x4>(v_in, lane);
         float w4[4] = {W[0], W[1], W[2], W[3]};
         float m4[4] = {M[0], M[1], M[2], M[3]};
         float v4[4] = {V[0], V[1], V[2], V[3]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) adam1(G[e], w4[e], m4[e], v4[e], k);
-        stg_nt<f32x4>(wp, lane, f32x4{w4[0], w4[1], w4[2], w4[3]});
-        stg_nt<f32x4>(mp, lane, f32x4{m4[0], m4[1], m4[2], m4[3]});
-        stg_nt<f32x4>(vp, lane, f32x4{v4[0], v4[1], v4[2], v4[3]});
-        const uint32_t p01 = static_cast<uint32_t>(narrow1<kParam>(w4[0])) |
-                             (static_cast<uint32_t>(narrow1<kParam>(w4[1])) << 16);
-        const uint32_t p23 = static_cast<uint32_t>(narrow1<kParam>(w4[2])) |
-                             (static_cast<uint32_t>(narrow1<kParam>(w4[3])) << 16);
-        stg_nt<u32x2>(pp, lane, u32x2{p01, p23});
+        stg_nt<f32x4>(w_out, lane, f32x4{w4[0], w4[1], w4[2], w4[3]});
+        stg_nt<f32x4>(m_out, lane, f32x4{m4[0], m4[1], m4[2], m4[3]});
+        stg_nt<f32x4>(v_out, lane, f32x4{v4[0], v4[1], v4[2], v4[3]});
+        stg_nt<u32x2>(p, lane, narrow4<kParam>(w4));
+    }
+
+    // element i with gradient g (per-element path)
+    template <int kParam>
+    __device__ __forceinline__ void update1(float g, int i, const AdamCoef& k) const {
+        float w = ldg<float>(w_in, i), m = ldg<float>(m_in, i), v = ldg<float>(v_in, i);
+        adam1(g, w, m, v, k);
+        stg<float>(w_out, i, w);
+        stg<float>(m_out, i, m);
+        stg<float>(v_out, i, v);
+        stg<uint16_t>(p, i, narrow1<kParam>(w));
+    }
+};
+
+// two-pass update, in place on the current bank, with the finalised scalars
+template <bool kFlat, int kParam>
+__global__ void __launch_bounds__(kWave) k_adamw(Table t, int64_t base, RoleRef gbar, StateRefs sr, RoleRef pr,
+                                                   const DevState* __restrict__ st, AdamArgs args) {
+    if (st->found_inf) return;
+    const AdamCoef k = adam_coef(st->gscale, st->beta1_pow, st->beta2_pow, args);
+    const int bank = st->bank;
+    const Piece q = piece_of<kFlat>(t, base + blockIdx.x);
+    const float* __restrict__ gp = elem_ptr<const float>(gbar, q);
+    const StatePtrs sp(sr, pr, bank, bank, q);
+    const LaneSpan l = lane_span(q);
+    if (l.full && sp.ok && aligned(gp, 16)) {
+        sp.update4<kParam>(ldg_nt<f32x4>(gp, threadIdx.x), threadIdx.x, k);
+    } else {
+        for (int i = l.lo; i < l.hi; ++i) sp.update1<kParam>(ldg<float>(gp, i), i, k);
+    }
+}
+
+// ============================================================================
+// single pass: replica average, statistics and the update of every element
+// in one read of the sources and the state.  Without clipping the update of
+// a step depends on the statistics only through the skip decision, so it is
+// computed with the scalars the step has if applied (gscale = 1 / scale, t + 1)
+// into the other bank; the finalisation makes that bank current only when the
+// step is applied.  Table pieces, as k_reduce, so the statistics are the same.
+// ============================================================================
+template <int kMode, int kGrad, int N, int kParam>
+__global__ void __launch_bounds__(kWave) k_reduce_adamw(Table t, int64_t base, Srcs accs, Srcs grads, StateRefs sr,
+                                                          RoleRef pr, StatsBuf sb, const DevState* __restrict__ st,
+                                                          AdamArgs args) {
+    AdamCoef k;
+    {
+#pragma clang fp contract(off)
+        k = adam_coef(1.0 / st->scale, st->beta1_pow * args.beta1, st->beta2_pow * args.beta2, args);
+    }
+    const int bank = st->bank;
+    const int64_t p = base + blockIdx.x;
+    const Piece q = piece_of<false>(t, p);
+    const ReduceSrc<kMode, kGrad, N> src(q, accs, grads);
+    const StatePtrs sp(sr, pr, bank, bank ^ 1, q);
+    const LaneSpan l = lane_span(q);
+    double ss = 0.0;
+    uint32_t bad = 0;
+    if (l.full && src.ok && sp.ok) {
+        const f32x4 y = src.vec(threadIdx.x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) add_stats(y[e], ss, bad);
+        sp.update4<kParam>(y, threadIdx.x, k);
     } else {
         for (int i = l.lo; i < l.hi; ++i) {
-            float w = ldg<float>(wp, i), m = ldg<float>(mp, i), v = ldg<float>(vp, i);
-            adam1(ldg<float>(gp, i), w, m, v, k);
-            stg<float>(wp, i, w);
-            stg<float>(mp, i, m);
-            stg<float>(vp, i, v);
-            stg<uint16_t>(pp, i, narrow1<kParam>(w));
+            const float y = src.elem(i);
+            add_stats(y, ss, bad);
+            sp.update1<kParam>(y, i, k);
+        }
+    }
+    wave_stats_store(ss, bad, p, t.npieces, sb);
+}
+
+// After a skipped single-pass step the parameters hold the discarded update:
+// emit them again from the current bank's master.  A grid-stride loop over the
+// pieces, so the launch costs a few microseconds when there is nothing to do.
+constexpr unsigned kRestoreBlocks = 4096;
+
+template <bool kFlat, int kParam>
+__global__ void __launch_bounds__(kWave) k_restore_param(Table t, StateRefs sr, RoleRef pr,
+                                                           const DevState* __restrict__ st) {
+    if (!st->found_inf) return;
+    const int bank = st->bank;
+    for (int64_t pc = blockIdx.x; pc < t.npieces; pc += gridDim.x) {
+        const Piece q = piece_of<kFlat>(t, pc);
+        const float* __restrict__ w = elem_ptr<const float>(sr.w[bank], q);
+        uint16_t* __restrict__ pp = elem_ptr<uint16_t>(pr, q);
+        const LaneSpan l = lane_span(q);
+        if (l.full && aligned(w, 16) && aligned(pp, 8)) {
+            const f32x4 W = ldg<f32x4>(w, threadIdx.x);
+            const float w4[4] = {W[0], W[1], W[2], W[3]};
+            stg<u32x2>(pp, threadIdx.x, narrow4<kParam>(w4));
+        } else {
+            for (int i = l.lo; i < l.hi; ++i) stg<uint16_t>(pp, i, narrow1<kParam>(ldg<float>(w, i)));
         }
     }
 }
@@ -590,14 +713,41 @@ hipError_t accumulate_all_t(dp_dtype gdt, bool first, int n, const Table& t, con
 }
 
 template <bool kFlat>
-hipError_t adamw_t(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
-                   const DevState* st, const AdamArgs& args, hipStream_t s) {
+hipError_t adamw_t(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& sr, RoleRef p, const DevState* st,
+                   const AdamArgs& args, hipStream_t s) {
     return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
         if (pdt == DP_BF16)
-            hipLaunchKernelGGL((k_adamw<kFlat, 2>), grid, dim3(kWave), 0, s, t, b, gbar, w, m, v, p, st, args);
+            hipLaunchKernelGGL((k_adamw<kFlat, 2>), grid, dim3(kWave), 0, s, t, b, gbar, sr, p, st, args);
         else
-            hipLaunchKernelGGL((k_adamw<kFlat, 1>), grid, dim3(kWave), 0, s, t, b, gbar, w, m, v, p, st, args);
+            hipLaunchKernelGGL((k_adamw<kFlat, 1>), grid, dim3(kWave), 0, s, t, b, gbar, sr, p, st, args);
     });
+}
+
+template <int kMode, int kGrad, int N>
+hipError_t reduce_adamw_n(dp_dtype pdt, const Table& t, const Srcs& accs, const Srcs& grads, const StateRefs& sr,
+                          RoleRef p, StatsBuf sb, const DevState* st, const AdamArgs& args, hipStream_t s) {
+    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+        if (pdt == DP_BF16)
+            hipLaunchKernelGGL((k_reduce_adamw<kMode, kGrad, N, 2>), grid, dim3(kWave), 0, s, t, b, accs, grads, sr,
+                               p, sb, st, args);
+        else
+            hipLaunchKernelGGL((k_reduce_adamw<kMode, kGrad, N, 1>), grid, dim3(kWave), 0, s, t, b, accs, grads, sr,
+                               p, sb, st, args);
+    });
+}
+
+template <int kMode, int kGrad>
+hipError_t reduce_adamw_dispatch(dp_dtype pdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
+                                 const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st,
+                                 const AdamArgs& args, hipStream_t s) {
+    switch (n) {
+#define DP_CASE(K) \
+    case K: return reduce_adamw_n<kMode, kGrad, K>(pdt, t, accs, grads, sr, p, sb, st, args, s);
+        DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
+        DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
+#undef DP_CASE
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -633,12 +783,13 @@ hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t s
 
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t s) {
-    if (nparts <= kFoldGroup) {
-        hipLaunchKernelGGL(k_finalize<uint32_t>, dim3(1), dim3(kFoldThreads), 0, s, sb.sumsq, sb.bad, nparts, st, args);
+    const int64_t nslots = nparts > 0 ? stats_slots(nparts) : 0;
+    if (nslots <= kFoldGroup) {
+        hipLaunchKernelGGL(k_finalize<uint32_t>, dim3(1), dim3(kFoldThreads), 0, s, sb.sumsq, sb.bad, nslots, st, args);
         return hipGetLastError();
     }
-    const int64_t groups = (nparts + kFoldGroup - 1) / kFoldGroup;
-    hipLaunchKernelGGL(k_fold, dim3(static_cast<unsigned>(groups)), dim3(kFoldThreads), 0, s, sb, nparts, fold);
+    const int64_t groups = (nslots + kFoldGroup - 1) / kFoldGroup;
+    hipLaunchKernelGGL(k_fold, dim3(static_cast<unsigned>(groups)), dim3(kFoldThreads), 0, s, sb, nslots, fold);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_finalize<uint64_t>, dim3(1), dim3(kFoldThreads), 0, s, fold.sumsq, fold.bad, groups, st,
@@ -646,10 +797,38 @@ hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* 
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, RoleRef w, RoleRef m, RoleRef v, RoleRef p,
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& sr, RoleRef p,
                         const DevState* st, const AdamArgs& args, hipStream_t s) {
-    return t.flat ? adamw_t<true>(pdt, t, gbar, w, m, v, p, st, args, s)
-                  : adamw_t<false>(pdt, t, gbar, w, m, v, p, st, args, s);
+    return t.flat ? adamw_t<true>(pdt, t, gbar, sr, p, st, args, s) : adamw_t<false>(pdt, t, gbar, sr, p, st, args, s);
+}
+
+hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, const Srcs& accs,
+                               const Srcs& grads, const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st,
+                               const AdamArgs& args, hipStream_t s) {
+    if (t.flat) return hipErrorInvalidValue;  // statistics: table pieces
+    if (mode == ReduceMode::kGradients) {
+        if (gdt == DP_F16) return reduce_adamw_dispatch<1, 1>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+        return reduce_adamw_dispatch<1, 2>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+    }
+    if (mode == ReduceMode::kAccPlusGrad) {
+        if (gdt == DP_F16) return reduce_adamw_dispatch<2, 1>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+        return reduce_adamw_dispatch<2, 2>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& sr, RoleRef p, const DevState* st,
+                                hipStream_t s) {
+    if (t.npieces == 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(t.npieces < kRestoreBlocks ? t.npieces : kRestoreBlocks));
+    if (t.flat) {
+        if (pdt == DP_BF16) hipLaunchKernelGGL((k_restore_param<true, 2>), grid, dim3(kWave), 0, s, t, sr, p, st);
+        else hipLaunchKernelGGL((k_restore_param<true, 1>), grid, dim3(kWave), 0, s, t, sr, p, st);
+    } else {
+        if (pdt == DP_BF16) hipLaunchKernelGGL((k_restore_param<false, 2>), grid, dim3(kWave), 0, s, t, sr, p, st);
+        else hipLaunchKernelGGL((k_restore_param<false, 1>), grid, dim3(kWave), 0, s, t, sr, p, st);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t s) {

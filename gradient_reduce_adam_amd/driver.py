@@ -12,14 +12,18 @@ plan and issues one step as:
   statistics instead);
 
 then ``dp_grad_stats`` and one ``dp_adam_step`` per shard range.  Both
-sequences give the same bits.  Gradients come from a caller-supplied
-producer, standing in for the backward pass; the fused sequence needs the n
-replicas' gradients of one micro-step at once.
+sequences give the same bits.  With ``single_pass`` (runs without clipping)
+the last micro-step, the replica average, the statistics and the update are
+one ``dp_reduce_adam_step`` over two state banks; again the same bits.
+Gradients come from a caller-supplied producer, standing in for the backward
+pass; the fused sequence needs the n replicas' gradients of one micro-step at
+once.
 
 HBM layout (flat parameter space of P elements, tensors in list order):
-master, exp_avg, exp_avg_sq: binary32 [P]; param: bf16/fp16 [P];
-acc[r]: binary32 [P] per replica (absent for partials; with n = 1, acc[0] is
-also g_bar); gbar: binary32 [P] when n > 1 or with partials; gradients: the
+master, exp_avg, exp_avg_sq: binary32 [P] (two banks of each with
+``single_pass``); param: bf16/fp16 [P]; acc[r]: binary32 [P] per replica
+(absent for partials; with n = 1, acc[0] is also g_bar); gbar: binary32 [P]
+when n > 1 or with partials, and not with ``single_pass``; gradients: the
 producer's buffers, bound per call.
 """
 from __future__ import annotations
@@ -47,10 +51,17 @@ class DPStep:
                  beta2: float = 0.999, max_norm: float = 0.0, scaler: str = "none", init_scale: float = 1.0,
                  backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, partials: bool = False,
                  shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
-                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True):
+                 device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True,
+                 single_pass: bool = False):
         if partials and a != 1:
             raise ValueError("incoming partials are reduced directly: a must be 1")
-        self.n, self.a, self.partials, self.fused = n, a, partials, fused
+        if single_pass and max_norm > 0.0:
+            raise ValueError("the single pass updates before the global norm is known: it needs max_norm = 0")
+        if single_pass and not (fused or partials):
+            raise ValueError("the single pass reads every replica's last micro-step at once: it needs fused = True")
+        if single_pass and shards is not None and list(shards) != [(0, sum(numel))]:
+            raise ValueError("the single pass updates the whole range in one call")
+        self.n, self.a, self.partials, self.fused, self.single_pass = n, a, partials, fused, single_pass
         self.lr, self.eps, self.weight_decay, self.max_norm = lr, eps, weight_decay, max_norm
         self.scaler = scaler
         self.plan = Plan(numel, n, grad_dtype, param_dtype, chunk_elems)
@@ -63,15 +74,23 @@ class DPStep:
         self.exp_avg_sq = torch.zeros(P, **f32)
         self.param = torch.zeros(P, dtype=TORCH_DTYPES[param_dtype], device=self.device)
         self.acc: List[torch.Tensor] = [] if partials else [torch.zeros(P, **f32) for _ in range(n)]
-        self.gbar = self.acc[0] if (n == 1 and not partials) else torch.zeros(P, **f32)
+        if n == 1 and not partials:
+            self.gbar = self.acc[0]
+        else:
+            self.gbar = None if single_pass else torch.zeros(P, **f32)
+        # state banks: (master, exp_avg, exp_avg_sq); bank 1 only for the single pass
+        self.banks = [(self.master, self.exp_avg, self.exp_avg_sq)]
+        if single_pass:
+            self.banks.append(tuple(torch.zeros(P, **f32) for _ in range(3)))
         pl = self.plan
-        pl.bind("master", self.master)
-        pl.bind("exp_avg", self.exp_avg)
-        pl.bind("exp_avg_sq", self.exp_avg_sq)
+        for b, (w_, m_, v_) in enumerate(self.banks):
+            pl.bind("master", w_, b)
+            pl.bind("exp_avg", m_, b)
+            pl.bind("exp_avg_sq", v_, b)
         pl.bind("param", self.param)
         for r, t in enumerate(self.acc):
             pl.bind("acc", t, r)
-        if self.gbar is not (self.acc[0] if self.acc else None):
+        if self.gbar is not None and self.gbar is not (self.acc[0] if self.acc else None):
             pl.bind("gbar", self.gbar)
         self.shards = list(shards) if shards is not None else [(0, P)]
         for b, e in self.shards:
@@ -100,7 +119,8 @@ class DPStep:
                 pl.accumulate_all(first=(k == 1), stream=st)
             for r in range(self.n):
                 dp_plan_bind_flat(h, DP_ROLE_GRAD, r, produce(step, r, last, self.scale))
-            pl.accumulate_reduce(stream=st)
+            if not self.single_pass:  # else the reduction is part of finish()
+                pl.accumulate_reduce(stream=st)
             return
         for k in range(1, self.a + 1):
             for r in range(self.n):
@@ -112,6 +132,9 @@ class DPStep:
     def finish(self) -> None:
         """Statistics, scalars and the update on every shard range."""
         pl, st = self.plan, self.stream.cuda_stream
+        if self.single_pass:
+            pl.reduce_adam_step(self.lr, self.eps, self.weight_decay, stream=st)
+            return
         pl.grad_stats(scan=False, max_norm=self.max_norm, stream=st)
         for b, e in self.shards:
             pl.adam_step(self.lr, self.eps, self.weight_decay, b, e, stream=st)
@@ -128,6 +151,10 @@ class DPStep:
 
     def read_state(self) -> dict:
         return self.plan.read_state(stream=self.stream.cuda_stream)
+
+    def state_tensors(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        """(master, exp_avg, exp_avg_sq) of the current bank (synchronises)."""
+        return self.banks[self.read_state()["bank"]]
 
     def close(self) -> None:
         self.plan.close()

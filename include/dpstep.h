@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 1
+#define DP_ABI_VERSION 2
 #define DP_MAX_REPLICAS 16
 #define DP_DEFAULT_CHUNK 16384
 
@@ -63,12 +63,16 @@ typedef enum dp_status {
 
 typedef enum dp_dtype { DP_F32 = 0, DP_F16 = 1, DP_BF16 = 2 } dp_dtype;
 
-/* Memory roles.  All roles are laid out like the flat parameter space. */
+/* Memory roles.  All roles are laid out like the flat parameter space.
+ * MASTER, EXP_AVG and EXP_AVG_SQ have two banks (the replica argument of the
+ * bind calls, 0 or 1).  Bank 0 is required; bank 1 only by
+ * dp_reduce_adam_step, which reads the current bank and writes the other.
+ * dp_step_state.bank says which bank is current. */
 typedef enum dp_role {
     DP_ROLE_PARAM = 0,      /* low-precision parameters (param dtype); written by dp_adam_step */
-    DP_ROLE_MASTER = 1,     /* binary32 master weights */
-    DP_ROLE_EXP_AVG = 2,    /* binary32 first moment m */
-    DP_ROLE_EXP_AVG_SQ = 3, /* binary32 second moment v */
+    DP_ROLE_MASTER = 1,     /* binary32 master weights (two banks) */
+    DP_ROLE_EXP_AVG = 2,    /* binary32 first moment m (two banks) */
+    DP_ROLE_EXP_AVG_SQ = 3, /* binary32 second moment v (two banks) */
     DP_ROLE_GRAD = 4,       /* per replica: the micro-step gradient, or the incoming partial (grad dtype) */
     DP_ROLE_ACC = 5,        /* per replica: binary32 accumulator g_r */
     DP_ROLE_GBAR = 6        /* binary32 averaged gradient g_bar; with n = 1 it defaults to ACC[0] */
@@ -115,7 +119,7 @@ typedef struct dp_step_state {
     double beta2_pow;        /* beta2^t */
     double scale;            /* loss scale the next step's gradients must carry */
     int32_t found_inf;       /* the last finalised g_bar held an inf or NaN: the step was skipped */
-    int32_t reserved;
+    int32_t bank;            /* state bank (0 or 1) holding the current master, m and v */
     double sumsq;            /* sum of squares of the last (scaled) g_bar */
     double norm;             /* L2 norm of the last unscaled g_bar */
     double clip;             /* global-norm clip factor applied (1 when off or not needed) */
@@ -138,6 +142,10 @@ typedef struct dp_plan_info {
     double bytes_accumulate_reduce; /* read n accumulators and n gradients, write g_bar */
     double bytes_stats_scan;        /* read g_bar */
     double bytes_adam;              /* read g_bar, w, m, v; write w, m, v, p */
+    /* dp_reduce_adam_step: read n accumulators and n gradients (or n
+     * partials), w, m, v; write w, m, v, p (g_bar is not stored) */
+    double bytes_reduce_adam;
+    double bytes_reduce_adam_partials;
 } dp_plan_info;
 
 /* One entry of a chunk table: a piece of one tensor, at most chunk_elems long. */
@@ -174,9 +182,9 @@ dp_status dp_plan_chunks(const dp_plan* plan, int64_t begin, int64_t end, int64_
                          dp_chunk* out, int64_t* count);
 
 /* Binds one contiguous device buffer to a role: tensor i starts at element
- * prefix[i] of it.  replica selects the GRAD / ACC buffer (0 for the other
- * roles).  Host work only; rebinding is cheap and may happen between any two
- * calls. */
+ * prefix[i] of it.  replica selects the GRAD / ACC buffer, or the bank (0, 1)
+ * of MASTER / EXP_AVG / EXP_AVG_SQ; 0 for PARAM and GBAR.  Host work only;
+ * rebinding is cheap and may happen between any two calls. */
 dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* device_base);
 
 /* Binds one device pointer per tensor (host array ptrs[num_tensors]).  The
@@ -253,6 +261,32 @@ dp_status dp_grad_stats(dp_plan* plan, int32_t scan, double max_norm, hipStream_
  * that dp_plan_prepare_range did not prepare allocates its table. */
 dp_status dp_adam_step(dp_plan* plan, const dp_adam_hparams* hp, int64_t shard_begin, int64_t shard_end,
                        hipStream_t stream);
+
+/* The whole step after the micro-steps, in one pass over memory, for runs
+ * without gradient clipping.  It reads the sources of dp_accumulate_reduce
+ * (ACC[r] + GRAD[r], or GRAD[r] alone with no earlier micro-step since the last
+ * reduction) and the current state bank once.  It writes the other bank and
+ * PARAM once.  g_bar is never stored.
+ *
+ * Without clipping, the statistics of g_bar change the update only through the
+ * skip decision [first page, loss scaling as part of the training state].  So
+ * every element's update is computed before that decision is known, with the
+ * scalars the step has if it is applied: gscale = 1 / scale and t + 1.  The
+ * finalisation of dp_grad_stats(scan = 0, max_norm = 0) then runs on the
+ * device.  If the step is applied, the written bank becomes current.  If it is
+ * skipped, the current bank stays as it was and PARAM is emitted again from
+ * its master.
+ *
+ * The result, bit for bit, is that of dp_accumulate_reduce, dp_grad_stats(0,
+ * 0) and dp_adam_step over [0, P): the same state and the same scalars.  This
+ * assumes PARAM held the round-to-nearest-even image of the current master
+ * before the call, as dp_adam_step leaves it.
+ *
+ * Needs both banks of MASTER, EXP_AVG and EXP_AVG_SQ (DP_ERR_UNBOUND).
+ * DP_ERR_STATE if the replicas are at different micro-steps or before
+ * dp_state_init.  Afterwards dp_adam_step returns DP_ERR_STATE until the next
+ * step's statistics. */
+dp_status dp_reduce_adam_step(dp_plan* plan, const dp_adam_hparams* hp, hipStream_t stream);
 
 /* Copies the device scalar state into host struct out after the stream's
  * previous work (synchronises the stream). */

@@ -38,13 +38,13 @@ def log(msg: str) -> None:
 class GpuRun:
     """A workload on the GPU: the library's driver plus device-generated inputs."""
 
-    def __init__(self, w, shards=None, chunk_elems: int = 0, fused: bool = True):
+    def __init__(self, w, shards=None, chunk_elems: int = 0, fused: bool = True, single_pass: bool = False):
         self.w = w
         self.d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                                weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                                scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                                growth_interval=w.growth_interval, partials=w.partials, shards=shards,
-                               chunk_elems=chunk_elems, fused=fused)
+                               chunk_elems=chunk_elems, fused=fused, single_pass=single_pass)
         slots = w.n if (w.partials or fused) else 1  # the fused step holds every replica's gradient at once
         self.slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(slots)]
         self.stream = self.d.stream.cuda_stream
@@ -67,11 +67,15 @@ class GpuRun:
         return self.states
 
     def window(self, lo: int, hi: int) -> Dict[str, np.ndarray]:
+        """master, m, v (of the current state bank), p and, when the run
+        stores it, g_bar over [lo, hi)."""
         torch.cuda.synchronize()
-        return {"w": self.d.master[lo:hi].cpu().numpy(), "m": self.d.exp_avg[lo:hi].cpu().numpy(),
-                "v": self.d.exp_avg_sq[lo:hi].cpu().numpy(),
-                "p": self.d.param[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16),
-                "gbar": self.d.gbar[lo:hi].cpu().numpy()}
+        w_, m_, v_ = self.d.state_tensors()
+        out = {"w": w_[lo:hi].cpu().numpy(), "m": m_[lo:hi].cpu().numpy(), "v": v_[lo:hi].cpu().numpy(),
+               "p": self.d.param[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16)}
+        if self.d.gbar is not None:
+            out["gbar"] = self.d.gbar[lo:hi].cpu().numpy()
+        return out
 
     def close(self):
         self.d.close()

@@ -22,14 +22,14 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert sorted(dp.EXPORTS) == names
     for n in names:
         assert hasattr(dp.lib, n), n
 
 
 def test_abi_version_and_status_strings():
-    assert dp.dp_abi_version() == 1
+    assert dp.dp_abi_version() == 2
     assert dp.dp_status_string(dp.DP_ERR_RANGE) == "range out of bounds"
     assert dp.dp_status_string(0) == "ok"
 
@@ -101,6 +101,8 @@ def test_plan_info_byte_model():
         assert info["bytes_reduce_acc"] == (4 * 8 + 4) * P and info["bytes_reduce_partials"] == (2 * 8 + 4) * P
         assert info["bytes_adam"] == 30 * P and info["bytes_stats_scan"] == 4 * P
         assert info["bytes_accumulate_reduce"] == ((2 + 4) * 8 + 4) * P
+        assert info["bytes_reduce_adam"] == ((2 + 4) * 8 + 26) * P
+        assert info["bytes_reduce_adam_partials"] == (2 * 8 + 26) * P
         assert info["num_chunks"] == len(p.chunks())
 
 
@@ -114,7 +116,10 @@ def test_bind_and_call_errors_before_any_launch():
             dp.dp_plan_bind_flat(h, dp.DP_ROLE_ACC, 2, 0x1000)
         assert e.value.status == dp.DP_ERR_INVALID_ARG
         with pytest.raises(dp.DpError) as e:
-            dp.dp_plan_bind_flat(h, dp.DP_ROLE_MASTER, 1, 0x1000)  # only GRAD / ACC are per replica
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_MASTER, 2, 0x1000)  # two banks only
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_PARAM, 1, 0x1000)  # one PARAM buffer
         assert e.value.status == dp.DP_ERR_INVALID_ARG
         with pytest.raises(dp.DpError) as e:
             dp.dp_accumulate(h, 0, True, stream=0)
@@ -155,6 +160,12 @@ def test_bind_and_call_errors_before_any_launch():
         with pytest.raises(dp.DpError) as e:
             dp.dp_adam_step(h, 1e-3, 1e-8, 0.0, 0, 10, stream=0)  # no statistics yet
         assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_adam_step(h, 1e-3, 1e-8, 0.0, stream=0)  # before dp_state_init
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_adam_step(h, 1e-3, -1.0, 0.0, stream=0)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
         with pytest.raises(dp.DpError) as e:
             dp.dp_read_state(h, stream=0)
         assert e.value.status == dp.DP_ERR_STATE

@@ -93,10 +93,11 @@ def test_partials_reduction_bit_exact():
 # ----------------------------------------------------------------------------
 # whole runs, every element
 # ----------------------------------------------------------------------------
-def _full_parity(w, steps, shards=None, chunk=0, label=""):
+def _full_parity(w, steps, shards=None, chunk=0, label="", single_pass=False):
     log(f"full parity {label or w.name}: P={w.P} T={w.T} n={w.n} a={w.a} {w.grad_dtype}/{w.param_dtype} "
-        f"clip={w.max_norm} scaler={w.scaler} steps={steps} shards={0 if shards is None else len(shards)}")
-    run = GpuRun(w, shards=shards, chunk_elems=chunk)
+        f"clip={w.max_norm} scaler={w.scaler} steps={steps} shards={0 if shards is None else len(shards)} "
+        f"single_pass={single_pass}")
+    run = GpuRun(w, shards=shards, chunk_elems=chunk, single_pass=single_pass)
     try:
         gpu_states = run.run(steps)
         got = run.window(0, w.P)
@@ -179,6 +180,83 @@ def test_per_replica_sequence_equals_fused_bitwise(name):
     for x, y in zip(sa, sb):  # same bits, NaN statistics of skipped steps included
         assert np.array_equal(np.array(list(x.values()), np.float64).view(np.uint64),
                               np.array(list(y.values()), np.float64).view(np.uint64))
+
+
+# ----------------------------------------------------------------------------
+# the single pass (reduce + statistics + update in one read of the state,
+# committed after the skip decision) against the oracle and against the
+# two-pass sequence, bit for bit
+# ----------------------------------------------------------------------------
+SINGLE_PASS = {
+    # accumulators + last micro-step, fp16, four replicas: the tiny workload's shape, ragged
+    "acc_f16_n4": dict(base="tiny", numel=RAGGED, n=4, a=3, steps=4),
+    # incoming partials under a dynamic scale: skipped steps (NaN, +inf and -inf), growth
+    "dynamic_partials": dict(VARIANTS["dynamic_partials"]),
+    # one replica, four micro-steps, bf16, small chunks
+    "n1_bf16": dict(base="unsharded_7b", numel=RAGGED, n=1, a=4, chunk=256, steps=4),
+    # sixteen single-micro-step replicas
+    "n16": dict(VARIANTS["n16"]),
+    "bf16_grad_f16_param": dict(VARIANTS["bf16_grad_f16_param"]),
+}
+
+
+def _spec(table, name):
+    spec = dict(table[name])
+    base = workloads.by_name(spec.pop("base"))
+    chunk = spec.pop("chunk", 0)
+    steps = spec.pop("steps")
+    return base.with_(**spec), chunk, steps
+
+
+@pytest.mark.parametrize("name", sorted(SINGLE_PASS))
+def test_single_pass_full_parity(name):
+    w, chunk, steps = _spec(SINGLE_PASS, name)
+    _full_parity(w, steps, chunk=chunk, label="single pass " + name, single_pass=True)
+
+
+@pytest.mark.parametrize("name", sorted(SINGLE_PASS))
+def test_single_pass_equals_two_pass_bitwise(name):
+    w, chunk, steps = _spec(SINGLE_PASS, name)
+    log(f"single pass vs two passes {name}")
+    outs = []
+    for single in (False, True):
+        run = GpuRun(w, chunk_elems=chunk, single_pass=single)
+        try:
+            st = run.run(steps)
+            outs.append((run.window(0, w.P), st))
+        finally:
+            run.close()
+    (a, sa), (b, sb) = outs
+    for k in ("w", "m", "v", "p"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    for x, y in zip(sa, sb):  # every scalar but the bank index, bit for bit
+        keys = [k for k in x if k != "bank"]
+        assert np.array_equal(np.array([x[k] for k in keys], np.float64).view(np.uint64),
+                              np.array([y[k] for k in keys], np.float64).view(np.uint64))
+    # the banks alternate with the applied steps only
+    applied = sum(1 for s in sb if not s["found_inf"])
+    assert sb[-1]["bank"] == applied % 2 and sa[-1]["bank"] == 0
+
+
+def test_single_pass_skip_leaves_state_and_params_unchanged():
+    """A non-finite g_bar discards the speculative update: the current bank,
+    the parameters and every scalar but iter and the scale stay as they were."""
+    w = workloads.zero3_rank_7b().with_(numel=(70001, 3000), n=3, injections=((2, 1, 1, 4321, float("inf")),))
+    run = GpuRun(w, single_pass=True)
+    try:
+        s1 = run.step()
+        before = run.window(0, w.P)
+        s2 = run.step()
+        after = run.window(0, w.P)
+        assert s1["found_inf"] == 0 and s2["found_inf"] == 1
+        assert s2["bank"] == s1["bank"] == 1 and s2["t"] == s1["t"] == 1 and s2["iter"] == 2
+        assert s2["scale"] == s1["scale"] * w.backoff
+        for k in ("w", "m", "v", "p"):
+            assert np.array_equal(before[k].view(np.uint8), after[k].view(np.uint8)), k
+        s3 = run.step()
+        assert s3["found_inf"] == 0 and s3["bank"] == 0 and s3["t"] == 2
+    finally:
+        run.close()
 
 
 def test_sharded_update_equals_unsharded_bitwise():
@@ -359,6 +437,21 @@ def test_empty_plan_and_empty_tensors():
         assert st["t"] == 1 and st["found_inf"] == 0 and st["norm"] == 0.0
     w = workloads.tiny().with_(numel=(0, 5000, 0, 0, 3, 0), n=2, a=2, steps=2)
     _full_parity(w, 2, label="zero-size tensors")
+
+
+def test_single_pass_empty_plan():
+    s = torch.cuda.current_stream().cuda_stream
+    with dp.Plan((), 3, "bf16", "bf16") as p:
+        for role in ("master", "exp_avg", "exp_avg_sq"):
+            p.bind(role, 0, 0)
+            p.bind(role, 0, 1)
+        p.bind("param", 0)
+        for r in range(3):
+            p.bind("grad", 0, r)
+        p.state_init(stream=s)
+        p.reduce_adam_step(1e-3, 1e-8, 0.0, stream=s)
+        st = p.read_state(stream=s)
+        assert st["t"] == 1 and st["found_inf"] == 0 and st["norm"] == 0.0 and st["bank"] == 1
 
 
 def test_empty_shard_is_a_noop():
