@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 RESIDENT_GRAD_BUDGET = 80e9  # bytes of pre-generated gradients kept in HBM
+CPU_BASELINE_SECONDS = 10.0  # oracle work timed for the CPU baseline
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = (os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip"),
               os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "dp_internal.h"))
@@ -39,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="gpt2_small",
                     help="tiny | gpt2_small | zero3_rank_7b | unsharded_7b | tp_column_slice")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 22, help="params in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="params in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
     ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
@@ -291,12 +293,20 @@ def cpu_baseline(w, sample: int) -> dict:
     def grad_fn(step, r, k, lo, hi, sc):
         return pre[(r, k)][lo:hi]
 
-    t0 = time.perf_counter()
+    # one untimed step, then runs of steps (the same batch each step) until
+    # about ten seconds of oracle work are timed
     oracle.run(ws, 1, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
-    dt = time.perf_counter() - t0
-    return {"value": sample / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of {ws.name} (n={ws.n}, a={ws.a}) over {sample} params in one tensor, "
-                      f"{dt:.2f} s"}
+    steps, dt, k = 0, 0.0, 1
+    while dt < CPU_BASELINE_SECONDS:
+        t0 = time.perf_counter()
+        oracle.run(ws, k, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
+        dt += time.perf_counter() - t0
+        steps += k
+        k = max(1, min(200, int(math.ceil((CPU_BASELINE_SECONDS - dt) * steps / dt))))
+    return {"value": sample * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full steps of {ws.name} (n={ws.n}, a={ws.a}, every micro-step, the replica tree, "
+                      f"statistics and update) over {sample} params in one tensor, one pre-generated batch, "
+                      f"{dt:.1f} s"}
 
 
 def main():
