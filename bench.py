@@ -50,6 +50,9 @@ def parse():
                     help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
                          "update in one read of the state (runs without clipping); auto: single-pass when the "
                          "workload does not clip")
+    ap.add_argument("--checkpoint-dir", default="", metavar="DIR",
+                    help="after the timed steps, save the state to DIR as 8 shards and restore it as 4, and print "
+                         "a second JSON line with the save and restore rates")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -169,7 +172,31 @@ def launch_bytes(w, kind: str, single: bool = False) -> float:
     return w.P * per[kind] / launches.get(kind, 1)
 
 
-def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False):
+def measure_checkpoint(d, directory: str) -> dict:
+    """Save the state (current bank of master, m, v and the parameters) as 8
+    shards and commit, then restore it as 4 shards; rates in state bytes per
+    second, device memory to files and back."""
+    import torch
+
+    os.makedirs(directory, exist_ok=True)
+    P = d.P
+    state_bytes = P * (12 + 2)
+    cut = lambda k: [(P * i // k, P * (i + 1) // k) for i in range(k)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    d.save_checkpoint(directory, 1, ranges=cut(8))
+    t_save = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    d.load_checkpoint(directory, ranges=cut(4))
+    torch.cuda.synchronize()
+    t_load = time.perf_counter() - t0
+    return {"metric": "checkpoint save (8 shards) and restore (4 shards) of the step's state",
+            "state_bytes": state_bytes, "save_s": t_save, "load_s": t_load,
+            "save_gbps": state_bytes / t_save / 1e9, "load_gbps": state_bytes / t_load / 1e9, "unit": "GB/s"}
+
+
+def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
+            ckpt_dir: str = ""):
     import torch
 
     import synth
@@ -264,6 +291,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     state = d.read_state()
+    ckpt = measure_checkpoint(d, ckpt_dir) if ckpt_dir else None
     per_kind = {}
     for kind, pairs in events.items():
         ms = [a.elapsed_time(b) for a, b in pairs]
@@ -271,7 +299,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     d.close()
     del bufs
     torch.cuda.empty_cache()
-    return elapsed, per_kind, state
+    return elapsed, per_kind, state, ckpt
 
 
 def cpu_baseline(w, sample: int) -> dict:
@@ -330,8 +358,8 @@ def main():
         return
     w = workloads.by_name(args.workload)
     single = single_pass_for(w, args.update)
-    elapsed, per_kind, state = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration, args.bind,
-                                       single)
+    elapsed, per_kind, state, ckpt = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
+                                             args.bind, single, args.checkpoint_dir)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
@@ -384,6 +412,9 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(line), flush=True)
+    if ckpt:
+        ckpt["config"] = {"workload": w.name, "params": w.P}
+        print(json.dumps(ckpt), flush=True)
 
 
 if __name__ == "__main__":

@@ -22,7 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdpstep.so")
 
 # enums of dpstep.h
-DP_OK, DP_ERR_INVALID_ARG, DP_ERR_BAD_LAYOUT, DP_ERR_UNBOUND, DP_ERR_RANGE, DP_ERR_STATE, DP_ERR_OOM, DP_ERR_HIP = range(8)
+(DP_OK, DP_ERR_INVALID_ARG, DP_ERR_BAD_LAYOUT, DP_ERR_UNBOUND, DP_ERR_RANGE, DP_ERR_STATE, DP_ERR_OOM, DP_ERR_HIP,
+ DP_ERR_IO, DP_ERR_CORRUPT) = range(10)
 DP_F32, DP_F16, DP_BF16 = 0, 1, 2
 (DP_ROLE_PARAM, DP_ROLE_MASTER, DP_ROLE_EXP_AVG, DP_ROLE_EXP_AVG_SQ, DP_ROLE_GRAD, DP_ROLE_ACC,
  DP_ROLE_GBAR) = range(7)
@@ -39,7 +40,9 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
-           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state")
+           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state",
+           "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
+           "dp_checkpoint_load")
 
 
 class Layout(ctypes.Structure):
@@ -148,6 +151,15 @@ def _load():
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
         "dp_reduce_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), vp]),
         "dp_read_state": (ctypes.c_int, [vp, ctypes.POINTER(StepState), vp]),
+        "dp_ckpt_write_shard": (ctypes.c_int, [ctypes.c_char_p, i64, ctypes.POINTER(Layout), i64, i64, vp, vp, vp,
+                                               vp]),
+        "dp_ckpt_commit": (ctypes.c_int, [ctypes.c_char_p, i64, ctypes.POINTER(Layout), ctypes.POINTER(StepState),
+                                          ctypes.POINTER(StateCfg)]),
+        "dp_ckpt_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(Layout), i64, i64, vp, vp, vp, vp,
+                                        ctypes.POINTER(StepState), ctypes.POINTER(StateCfg), ctypes.POINTER(i64)]),
+        "dp_checkpoint_save": (ctypes.c_int, [vp, ctypes.c_char_p, i64, i64, i64, vp]),
+        "dp_checkpoint_commit": (ctypes.c_int, [vp, ctypes.c_char_p, i64, vp]),
+        "dp_checkpoint_load": (ctypes.c_int, [vp, ctypes.c_char_p, i64, i64, i32, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -286,6 +298,87 @@ def dp_read_state(plan: int, stream=None) -> dict:
 
 
 # ----------------------------------------------------------------------------
+# checkpoints (dpckpt.h): host layer on numpy arrays, device layer on a plan
+# ----------------------------------------------------------------------------
+PARAM_NP = {"bf16": np.uint16, "f16": np.uint16}
+
+
+def _layout(numel: Sequence[int], param_dtype: str):
+    arr = (ctypes.c_int64 * max(len(numel), 1))(*[int(x) for x in numel])
+    return Layout(len(numel), 1, arr, DP_BF16, DTYPES[param_dtype], 0, 0), arr
+
+
+def _f32c(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def dp_ckpt_write_shard(directory: str, generation: int, numel: Sequence[int], param_dtype: str, begin: int,
+                        end: int, master, exp_avg, exp_avg_sq, param) -> None:
+    lay, keep = _layout(numel, param_dtype)
+    arrs = [_f32c(master), _f32c(exp_avg), _f32c(exp_avg_sq), np.ascontiguousarray(param, dtype=np.uint16)]
+    for a in arrs:
+        if a.size != end - begin:
+            raise ValueError(f"arrays must hold end - begin = {end - begin} elements, got {a.size}")
+    ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in arrs]
+    _check(lib.dp_ckpt_write_shard(os.fsencode(directory), generation, ctypes.byref(lay), begin, end, *ptrs))
+
+
+def _state_struct(d: dict) -> "StepState":
+    st = StepState()
+    for k, _ in StepState._fields_:
+        if k in d:
+            setattr(st, k, d[k])
+    return st
+
+
+def dp_ckpt_commit(directory: str, generation: int, numel: Sequence[int], param_dtype: str, scalars: dict,
+                   cfg: dict) -> None:
+    lay, keep = _layout(numel, param_dtype)
+    st = _state_struct(scalars)
+    c = StateCfg(**cfg)
+    _check(lib.dp_ckpt_commit(os.fsencode(directory), generation, ctypes.byref(lay), ctypes.byref(st),
+                              ctypes.byref(c)))
+
+
+def dp_ckpt_read(directory: str, numel: Sequence[int], param_dtype: str, begin: int, end: int,
+                 arrays: bool = True) -> dict:
+    """{'master', 'exp_avg', 'exp_avg_sq', 'param' (uint16 bits): [begin, end),
+    'scalars': dict, 'cfg': dict, 'generation': int}"""
+    lay, keep = _layout(numel, param_dtype)
+    n = end - begin
+    out = {}
+    ptrs = [None] * 4
+    if arrays:
+        out = {"master": np.empty(n, np.float32), "exp_avg": np.empty(n, np.float32),
+               "exp_avg_sq": np.empty(n, np.float32), "param": np.empty(n, np.uint16)}
+        ptrs = [a.ctypes.data_as(ctypes.c_void_p) for a in out.values()]
+    st, c, gen = StepState(), StateCfg(), ctypes.c_int64()
+    _check(lib.dp_ckpt_read(os.fsencode(directory), ctypes.byref(lay), begin, end, *ptrs, ctypes.byref(st),
+                            ctypes.byref(c), ctypes.byref(gen)))
+    out["scalars"] = st.as_dict()
+    out["cfg"] = {k: getattr(c, k) for k, _ in StateCfg._fields_}
+    out["generation"] = int(gen.value)
+    return out
+
+
+def dp_checkpoint_save(plan: int, directory: str, generation: int, begin: int, end: int, stream=None) -> None:
+    _check(lib.dp_checkpoint_save(ctypes.c_void_p(plan), os.fsencode(directory), generation, begin, end,
+                                  ctypes.c_void_p(_stream(stream))))
+
+
+def dp_checkpoint_commit(plan: int, directory: str, generation: int, stream=None) -> None:
+    _check(lib.dp_checkpoint_commit(ctypes.c_void_p(plan), os.fsencode(directory), generation,
+                                    ctypes.c_void_p(_stream(stream))))
+
+
+def dp_checkpoint_load(plan: int, directory: str, begin: int, end: int, restore_scalars: bool,
+                       stream=None) -> None:
+    _check(lib.dp_checkpoint_load(ctypes.c_void_p(plan), os.fsencode(directory), begin, end,
+                                  int(bool(restore_scalars)), ctypes.c_void_p(_stream(stream))))
+
+
+# ----------------------------------------------------------------------------
 # object wrapper
 # ----------------------------------------------------------------------------
 class Plan:
@@ -359,3 +452,14 @@ class Plan:
 
     def read_state(self, stream=None) -> dict:
         return dp_read_state(self.handle, stream)
+
+    def checkpoint_save(self, directory: str, generation: int, begin: int = 0, end: Optional[int] = None,
+                        stream=None) -> None:
+        dp_checkpoint_save(self.handle, directory, generation, begin, self.P if end is None else end, stream)
+
+    def checkpoint_commit(self, directory: str, generation: int, stream=None) -> None:
+        dp_checkpoint_commit(self.handle, directory, generation, stream)
+
+    def checkpoint_load(self, directory: str, begin: int = 0, end: Optional[int] = None,
+                        restore_scalars: bool = True, stream=None) -> None:
+        dp_checkpoint_load(self.handle, directory, begin, self.P if end is None else end, restore_scalars, stream)

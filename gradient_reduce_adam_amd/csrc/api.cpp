@@ -14,8 +14,9 @@
 
 #include "dp_internal.h"
 #include "dpstep.h"
+#include "plan.h"
 
-namespace {
+namespace dpapi {
 
 thread_local std::string g_last_error;
 
@@ -33,31 +34,26 @@ dp_status hip_fail(hipError_t e, const char* what) {
     return fail(DP_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
 }
 
-constexpr int kNumRoles = 7;
+dp_status ensure_device(dp_plan* p) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (p->device >= 0 && p->device != dev)
+        return fail(DP_ERR_STATE, "plan was set up on device %d, current device is %d", p->device, dev);
+    p->device = dev;
+    return DP_OK;
+}
 
-struct Binding {
-    void* flat = nullptr;
-    std::vector<void*> tensors;
-    void** dev_table = nullptr;
-    bool bound = false;
+}  // namespace dpapi
 
-    dpk::RoleRef ref() const { return dpk::RoleRef{flat, dev_table}; }
-};
+using dpapi::Binding;
+using dpapi::DeviceTable;
+using dpapi::ensure_device;
+using dpapi::fail;
+using dpapi::hip_fail;
+using dpapi::kNumRoles;
 
-struct DeviceTable {
-    int64_t begin = 0, end = 0, count = 0;  // count: chunks
-    dp_chunk* dev = nullptr;
-    int log2s = 0;
-
-    // pieces of a launch over this range: direct flat pieces when every role
-    // of the call is flat-bound, else pieces of the chunks
-    int64_t npieces(bool flat) const {
-        if (!flat) return count << log2s;
-        const int64_t lo = begin & ~int64_t{3};
-        return end > begin ? (end - lo + dpk::kPiece - 1) / dpk::kPiece : 0;
-    }
-    dpk::Table table(bool flat) const { return dpk::Table{dev, begin, end, npieces(flat), log2s, flat}; }
-};
+namespace {
 
 int log2_exact(int64_t x) {
     int k = 0;
@@ -68,31 +64,6 @@ int log2_exact(int64_t x) {
 size_t esize(dp_dtype d) { return d == DP_F32 ? 4 : 2; }
 
 }  // namespace
-
-struct dp_plan {
-    std::vector<int64_t> numel, prefix;
-    int64_t P = 0;
-    int32_t T = 0, n = 1, chunk = DP_DEFAULT_CHUNK;
-    dp_dtype gdt = DP_BF16, pdt = DP_BF16;
-
-    Binding roles[kNumRoles][DP_MAX_REPLICAS];
-
-    // device resources (allocated by dp_state_init / prepare / bind_tensors)
-    int device = -1;
-    dpk::DevState* state = nullptr;
-    dpk::StatsBuf stats{nullptr, nullptr};
-    dpk::FoldBuf fold{nullptr, nullptr};
-    DeviceTable full;
-    std::vector<DeviceTable> ranges;
-
-    // ordering state
-    bool state_ready = false;
-    dp_state_cfg cfg{};
-    std::vector<int32_t> micro;   // micro-steps accumulated per replica since the last reduction
-    bool partials_valid = false;  // piece statistics of the current g_bar exist
-    int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
-    bool stats_current = false;   // dp_grad_stats ran on the current g_bar
-};
 
 namespace {
 
@@ -126,16 +97,6 @@ void build_chunks(const dp_plan* p, int64_t begin, int64_t end, std::vector<dp_c
             off = stop;
         }
     }
-}
-
-dp_status ensure_device(dp_plan* p) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (p->device >= 0 && p->device != dev)
-        return fail(DP_ERR_STATE, "plan was set up on device %d, current device is %d", p->device, dev);
-    p->device = dev;
-    return DP_OK;
 }
 
 dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out) {
@@ -237,11 +198,13 @@ const char* dp_status_string(dp_status s) {
         case DP_ERR_STATE: return "call out of order";
         case DP_ERR_OOM: return "out of memory";
         case DP_ERR_HIP: return "HIP error";
+        case DP_ERR_IO: return "file system error";
+        case DP_ERR_CORRUPT: return "checkpoint corrupt";
     }
     return "unknown status";
 }
 
-const char* dp_last_error(void) { return g_last_error.c_str(); }
+const char* dp_last_error(void) { return dpapi::g_last_error.c_str(); }
 
 dp_status dp_plan_create(const dp_layout* L, dp_plan** out) {
     if (!L || !out) return fail(DP_ERR_INVALID_ARG, "dp_plan_create: null argument");

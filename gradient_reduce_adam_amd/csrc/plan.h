@@ -1,0 +1,79 @@
+// The plan object behind the C ABI, shared by the files that implement it
+// (api.cpp: plans, bindings, the step; checkpoint.cpp: save and restore).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "dp_internal.h"
+#include "dpstep.h"
+
+namespace dpapi {
+
+constexpr int kNumRoles = 7;
+
+// Where one role's memory is: one flat buffer, or one pointer per tensor
+// (kept on the host and mirrored in a device table for the kernels).
+struct Binding {
+    void* flat = nullptr;
+    std::vector<void*> tensors;
+    void** dev_table = nullptr;
+    bool bound = false;
+
+    dpk::RoleRef ref() const { return dpk::RoleRef{flat, dev_table}; }
+};
+
+struct DeviceTable {
+    int64_t begin = 0, end = 0, count = 0;  // count: chunks
+    dp_chunk* dev = nullptr;
+    int log2s = 0;
+
+    // pieces of a launch over this range: direct flat pieces when every role
+    // of the call is flat-bound, else pieces of the chunks
+    int64_t npieces(bool flat) const {
+        if (!flat) return count << log2s;
+        const int64_t lo = begin & ~int64_t{3};
+        return end > begin ? (end - lo + dpk::kPiece - 1) / dpk::kPiece : 0;
+    }
+    dpk::Table table(bool flat) const { return dpk::Table{dev, begin, end, npieces(flat), log2s, flat}; }
+};
+
+// Records the message of a failure for dp_last_error() and returns s.
+dp_status fail(dp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dp_status hip_fail(hipError_t e, const char* what);
+extern thread_local std::string g_last_error;
+
+}  // namespace dpapi
+
+struct dp_plan {
+    std::vector<int64_t> numel, prefix;
+    int64_t P = 0;
+    int32_t T = 0, n = 1, chunk = DP_DEFAULT_CHUNK;
+    dp_dtype gdt = DP_BF16, pdt = DP_BF16;
+
+    dpapi::Binding roles[dpapi::kNumRoles][DP_MAX_REPLICAS];
+
+    // device resources (allocated by dp_state_init / prepare / bind_tensors)
+    int device = -1;
+    dpk::DevState* state = nullptr;
+    dpk::StatsBuf stats{nullptr, nullptr};
+    dpk::FoldBuf fold{nullptr, nullptr};
+    dpapi::DeviceTable full;
+    std::vector<dpapi::DeviceTable> ranges;
+
+    // ordering state
+    bool state_ready = false;
+    dp_state_cfg cfg{};
+    std::vector<int32_t> micro;   // micro-steps accumulated per replica since the last reduction
+    bool partials_valid = false;  // piece statistics of the current g_bar exist
+    int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
+    bool stats_current = false;   // dp_grad_stats ran on the current g_bar
+};
+
+namespace dpapi {
+// Binds the plan to the current device on first use; DP_ERR_STATE if another
+// device is current later.
+dp_status ensure_device(dp_plan* p);
+}  // namespace dpapi

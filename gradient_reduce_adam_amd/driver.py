@@ -152,6 +152,28 @@ class DPStep:
     def read_state(self) -> dict:
         return self.plan.read_state(stream=self.stream.cuda_stream)
 
+    # -- checkpoints (dpckpt.h) ---------------------------------------------
+    def save_checkpoint(self, directory: str, generation: int,
+                        ranges: Optional[Sequence[Tuple[int, int]]] = None) -> None:
+        """One shard file per range (default: the update's shard ranges), then
+        the commit of the generation."""
+        st = self.stream.cuda_stream
+        for b, e in (ranges if ranges is not None else self.shards):
+            self.plan.checkpoint_save(directory, generation, b, e, stream=st)
+        self.plan.checkpoint_commit(directory, generation, stream=st)
+
+    def load_checkpoint(self, directory: str, ranges: Optional[Sequence[Tuple[int, int]]] = None) -> dict:
+        """Restores the state over the given partition of [0, P) (default: the
+        update's shard ranges; any partition works) and resumes the step count
+        and the loss scale from it."""
+        st = self.stream.cuda_stream
+        for i, (b, e) in enumerate(ranges if ranges is not None else self.shards):
+            self.plan.checkpoint_load(directory, b, e, restore_scalars=(i == 0), stream=st)
+        s = self.read_state()
+        self.scale = s["scale"]
+        self.steps_done = s["iter"]
+        return s
+
     def state_tensors(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
         """(master, exp_avg, exp_avg_sq) of the current bank (synchronises)."""
         return self.banks[self.read_state()["bank"]]

@@ -58,7 +58,9 @@ typedef enum dp_status {
     DP_ERR_RANGE = 4,       /* range not inside [0, P) or begin > end */
     DP_ERR_STATE = 5,       /* call out of order (see each call) */
     DP_ERR_OOM = 6,         /* a library allocation failed */
-    DP_ERR_HIP = 7          /* a HIP call failed; dp_last_error() has its text */
+    DP_ERR_HIP = 7,         /* a HIP call failed; dp_last_error() has its text */
+    DP_ERR_IO = 8,          /* a file system call failed (dpckpt.h) */
+    DP_ERR_CORRUPT = 9      /* a checkpoint file failed its checks (dpckpt.h) */
 } dp_status;
 
 typedef enum dp_dtype { DP_F32 = 0, DP_F16 = 1, DP_BF16 = 2 } dp_dtype;
