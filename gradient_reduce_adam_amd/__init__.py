@@ -40,6 +40,7 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
+           "dp_accumulate_reduce_range",
            "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
            "dp_checkpoint_load")
@@ -146,6 +147,7 @@ def _load():
         "dp_accumulate": (ctypes.c_int, [vp, i32, i32, i32, vp]),
         "dp_accumulate_all": (ctypes.c_int, [vp, i32, vp]),
         "dp_accumulate_reduce": (ctypes.c_int, [vp, vp]),
+        "dp_accumulate_reduce_range": (ctypes.c_int, [vp, i64, i64, vp]),
         "dp_reduce_replicas": (ctypes.c_int, [vp, ctypes.c_int, vp]),
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
@@ -268,6 +270,10 @@ def dp_accumulate_all(plan: int, first: bool, stream=None) -> None:
 
 def dp_accumulate_reduce(plan: int, stream=None) -> None:
     _check(lib.dp_accumulate_reduce(ctypes.c_void_p(plan), ctypes.c_void_p(_stream(stream))))
+
+
+def dp_accumulate_reduce_range(plan: int, begin: int, end: int, stream=None) -> None:
+    _check(lib.dp_accumulate_reduce_range(ctypes.c_void_p(plan), begin, end, ctypes.c_void_p(_stream(stream))))
 
 
 def dp_reduce_replicas(plan: int, src: int = DP_ROLE_ACC, stream=None) -> None:
@@ -436,6 +442,9 @@ class Plan:
 
     def accumulate_reduce(self, stream=None) -> None:
         dp_accumulate_reduce(self.handle, stream)
+
+    def accumulate_reduce_range(self, begin: int, end: int, stream=None) -> None:
+        dp_accumulate_reduce_range(self.handle, begin, end, stream)
 
     def reduce_replicas(self, src: str = "acc", stream=None) -> None:
         dp_reduce_replicas(self.handle, ROLES[src], stream)

@@ -99,8 +99,10 @@ void build_chunks(const dp_plan* p, int64_t begin, int64_t end, std::vector<dp_c
     }
 }
 
-dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out) {
-    std::vector<dp_chunk> host;
+dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out,
+                       std::vector<dp_chunk>* keep = nullptr) {
+    std::vector<dp_chunk> tmp;
+    std::vector<dp_chunk>& host = keep ? *keep : tmp;
     build_chunks(p, begin, end, &host);
     out->begin = begin;
     out->end = end;
@@ -123,7 +125,7 @@ dp_status ensure_full(dp_plan* p) {
     if (p->full.dev || p->P == 0 || p->full.count > 0) return DP_OK;
     dp_status s = ensure_device(p);
     if (s != DP_OK) return s;
-    return upload_table(p, 0, p->P, &p->full);
+    return upload_table(p, 0, p->P, &p->full, &p->full_host);
 }
 
 dp_status range_table(dp_plan* p, int64_t begin, int64_t end, const DeviceTable** out) {
@@ -180,6 +182,31 @@ bool all_flat(const dpk::StateRefs& s) {
     for (int b = 0; b < 2; ++b)
         if (s.w[b].tab || s.m[b].tab || s.v[b].tab) return false;
     return true;
+}
+
+// Calls that start or end a reduction may not run while a bucketed one is
+// half done.
+dp_status no_open_buckets(const dp_plan* p, const char* where) {
+    if (!p->buckets.empty())
+        return fail(DP_ERR_STATE, "%s while a bucketed reduction covers %lld of %lld elements", where,
+                    static_cast<long long>(p->bucket_elems), static_cast<long long>(p->P));
+    return DP_OK;
+}
+
+// The piece of the [0, P) table that starts at flat element x, or -1 if no
+// piece starts there (x must be a tensor start, or a multiple of 256 elements
+// into its tensor); P maps to the table's end.
+int64_t piece_at(const dp_plan* p, int64_t x) {
+    const int64_t np = p->full.npieces(false);
+    if (x == p->P) return np;
+    const auto& ch = p->full_host;
+    const auto it = std::upper_bound(ch.begin(), ch.end(), x,
+                                     [](int64_t v, const dp_chunk& c) { return v < c.flat; });
+    if (it == ch.begin()) return -1;
+    const dp_chunk& c = *(it - 1);
+    const int64_t off = x - c.flat;
+    if (off >= c.len || off % dpk::kPiece != 0) return -1;
+    return (static_cast<int64_t>(it - 1 - ch.begin()) << p->full.log2s) + off / dpk::kPiece;
 }
 
 }  // namespace
@@ -403,11 +430,17 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     std::fill(p->micro.begin(), p->micro.end(), 0);
     p->partials_valid = false;
     p->stats_current = false;
+    p->buckets.clear();
+    p->bucket_elems = 0;
     return DP_OK;
 }
 
 dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit_stats, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate: null plan");
+    {
+        dp_status g = no_open_buckets(p, "dp_accumulate");
+        if (g != DP_OK) return g;
+    }
     if (replica < 0 || replica >= p->n) return fail(DP_ERR_INVALID_ARG, "replica %d outside [0, %d)", replica, p->n);
     if (emit_stats && p->n != 1)
         return fail(DP_ERR_INVALID_ARG, "emit_stats needs n_replicas == 1 (g_bar is then the accumulator)");
@@ -458,7 +491,8 @@ static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs
     if (s != DP_OK) return s;
     const dpk::Table t = p->full.table(false);  // statistics: table pieces
     if (t.npieces > 0) {
-        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, accs, grads, gb->ref(), p->stats, stream),
+        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{0, t.npieces}, accs, grads,
+                                            gb->ref(), p->stats, stream),
                          "reduce launch");
         if (s != DP_OK) return s;
     }
@@ -471,6 +505,10 @@ static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs
 
 dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_replicas: null plan");
+    {
+        dp_status g = no_open_buckets(p, "dp_reduce_replicas");
+        if (g != DP_OK) return g;
+    }
     if (src != DP_ROLE_ACC && src != DP_ROLE_GRAD)
         return fail(DP_ERR_INVALID_ARG, "src must be DP_ROLE_ACC or DP_ROLE_GRAD");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_replicas before dp_state_init");
@@ -489,6 +527,10 @@ dp_status dp_reduce_replicas(dp_plan* p, dp_role src, hipStream_t stream) {
 
 dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_all: null plan");
+    {
+        dp_status g = no_open_buckets(p, "dp_accumulate_all");
+        if (g != DP_OK) return g;
+    }
     dpk::Srcs grads{}, accs{};
     dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
     if (s == DP_OK) s = bound_replicas(p, DP_ROLE_ACC, &accs);
@@ -522,8 +564,69 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     return DP_OK;
 }
 
+dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce_range: null plan");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce_range before dp_state_init");
+    if (begin < 0 || end > p->P || begin > end)
+        return fail(DP_ERR_RANGE, "bucket [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
+                    static_cast<long long>(end), static_cast<long long>(p->P));
+    dp_status s = ensure_full(p);
+    if (s != DP_OK) return s;
+    const int64_t p0 = piece_at(p, begin), p1 = piece_at(p, end);
+    if (p0 < 0 || p1 < 0)
+        return fail(DP_ERR_INVALID_ARG,
+                    "bucket [%lld, %lld): each end must be a tensor start, P, or a multiple of 256 elements into "
+                    "its tensor",
+                    static_cast<long long>(begin), static_cast<long long>(end));
+    for (const auto& b : p->buckets)
+        if (begin < b.second && b.first < end)
+            return fail(DP_ERR_STATE, "bucket [%lld, %lld) overlaps bucket [%lld, %lld) of this reduction",
+                        static_cast<long long>(begin), static_cast<long long>(end),
+                        static_cast<long long>(b.first), static_cast<long long>(b.second));
+    const Binding* gb = gbar_binding(p);
+    if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
+    dpk::Srcs grads{}, accs{};
+    s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+    if (s != DP_OK) return s;
+    for (int32_t r = 0; r < p->n; ++r)
+        if (p->micro[r] != p->micro[0])
+            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
+                        p->micro[r], p->micro[0]);
+    const bool with_acc = p->micro[0] > 0;
+    if (with_acc) {
+        s = bound_replicas(p, DP_ROLE_ACC, &accs);
+        if (s != DP_OK) return s;
+    }
+    const dpk::Table t = p->full.table(false);  // statistics: table pieces, the slots of the whole reduction
+    if (p1 > p0) {
+        s = check_launch(dpk::launch_reduce(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
+                                            p->gdt, p->n, t, dpk::PieceSpan{p0, p1}, accs, grads, gb->ref(),
+                                            p->stats, stream),
+                         "reduce launch");
+        if (s != DP_OK) return s;
+    }
+    if (end > begin) {
+        p->buckets.emplace_back(begin, end);
+        p->bucket_elems += end - begin;
+    }
+    p->partials_valid = false;
+    p->stats_current = false;
+    if (p->bucket_elems == p->P) {  // the buckets cover [0, P): the reduction is complete
+        p->buckets.clear();
+        p->bucket_elems = 0;
+        std::fill(p->micro.begin(), p->micro.end(), 0);
+        p->partials_valid = true;
+        p->partials_count = t.npieces;
+    }
+    return DP_OK;
+}
+
 dp_status dp_accumulate_reduce(dp_plan* p, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce: null plan");
+    {
+        dp_status g = no_open_buckets(p, "dp_accumulate_reduce");
+        if (g != DP_OK) return g;
+    }
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce before dp_state_init");
     dpk::Srcs grads{}, accs{};
     dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
@@ -543,6 +646,10 @@ dp_status dp_accumulate_reduce(dp_plan* p, hipStream_t stream) {
 
 dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_grad_stats: null plan");
+    {
+        dp_status g = no_open_buckets(p, "dp_grad_stats");
+        if (g != DP_OK) return g;
+    }
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_grad_stats before dp_state_init");
     if (!(max_norm >= 0.0)) return fail(DP_ERR_INVALID_ARG, "max_norm must be >= 0 (0 disables clipping)");
     dp_status s = ensure_full(p);
@@ -600,6 +707,10 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
 
 dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t stream) {
     if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_step: null argument");
+    {
+        dp_status g = no_open_buckets(p, "dp_reduce_adam_step");
+        if (g != DP_OK) return g;
+    }
     if (!(hp->lr >= 0.0) || !(hp->eps > 0.0) || !(hp->weight_decay >= 0.0))
         return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_step before dp_state_init");

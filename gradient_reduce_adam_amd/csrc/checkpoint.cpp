@@ -794,6 +794,8 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
     std::fill(p->micro.begin(), p->micro.end(), 0);
     p->partials_valid = false;
     p->stats_current = false;
+    p->buckets.clear();
+    p->bucket_elems = 0;
     return DP_OK;
 }
 

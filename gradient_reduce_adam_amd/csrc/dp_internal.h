@@ -100,8 +100,12 @@ enum class ReduceMode {
     kGradients,     // g_r (the gradient dtype): partials, or a single micro-step
     kAccPlusGrad    // acc_r + g_r: the last micro-step fused, acc_r not written back
 };
-hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
-                         RoleRef gbar, StatsBuf sb, hipStream_t stream);
+// Pieces [p0, p1) of a table: the whole table, or one bucket of it.
+struct PieceSpan {
+    int64_t p0, p1;
+};
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,
+                         const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t stream);

@@ -631,12 +631,13 @@ __global__ void __launch_bounds__(kWave) k_restore_param(Table t, StateRefs sr, 
 }
 
 // ---- launch helpers ---------------------------------------------------------
-// Launches `launch(base, grid)` over npieces workgroups in slices of at most
-// kMaxBlocksPerLaunch (gridDim.y = ny).
+// Launches `launch(base, grid)` over pieces [p0, p1), one workgroup each, in
+// slices of at most kMaxBlocksPerLaunch (gridDim.y = ny); base is the piece
+// of the slice's first workgroup.
 template <typename F>
-hipError_t for_pieces(int64_t npieces, unsigned ny, F&& launch) {
-    for (int64_t b = 0; b < npieces; b += kMaxBlocksPerLaunch) {
-        const int64_t cnt = npieces - b < kMaxBlocksPerLaunch ? npieces - b : kMaxBlocksPerLaunch;
+hipError_t for_span(int64_t p0, int64_t p1, unsigned ny, F&& launch) {
+    for (int64_t b = p0; b < p1; b += kMaxBlocksPerLaunch) {
+        const int64_t cnt = p1 - b < kMaxBlocksPerLaunch ? p1 - b : kMaxBlocksPerLaunch;
         launch(b, dim3(static_cast<unsigned>(cnt), ny));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -644,19 +645,25 @@ hipError_t for_pieces(int64_t npieces, unsigned ny, F&& launch) {
     return hipSuccess;
 }
 
+template <typename F>
+hipError_t for_pieces(int64_t npieces, unsigned ny, F&& launch) {
+    return for_span(0, npieces, ny, static_cast<F&&>(launch));
+}
+
 template <bool kFlat, int kMode, int kGrad, int N>
-hipError_t reduce_n(const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+hipError_t reduce_n(const Table& t, PieceSpan sp, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb,
+                    hipStream_t s) {
+    return for_span(sp.p0, sp.p1, 1, [&](int64_t b, dim3 grid) {
         hipLaunchKernelGGL((k_reduce<kFlat, kMode, kGrad, N>), grid, dim3(kWave), 0, s, t, b, accs, grads, gbar, sb);
     });
 }
 
 template <bool kFlat, int kMode, int kGrad>
-hipError_t reduce_dispatch(int n, const Table& t, const Srcs& accs, const Srcs& grads, RoleRef gbar, StatsBuf sb,
-                           hipStream_t s) {
+hipError_t reduce_dispatch(int n, const Table& t, PieceSpan sp, const Srcs& accs, const Srcs& grads, RoleRef gbar,
+                           StatsBuf sb, hipStream_t s) {
     switch (n) {
 #define DP_CASE(K) \
-    case K: return reduce_n<kFlat, kMode, kGrad, K>(t, accs, grads, gbar, sb, s);
+    case K: return reduce_n<kFlat, kMode, kGrad, K>(t, sp, accs, grads, gbar, sb, s);
         DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
         DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
 #undef DP_CASE
@@ -665,15 +672,15 @@ hipError_t reduce_dispatch(int n, const Table& t, const Srcs& accs, const Srcs& 
 }
 
 template <bool kFlat>
-hipError_t reduce_modes(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
-                        RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<kFlat, 0, 2>(n, t, accs, grads, gbar, sb, s);
+hipError_t reduce_modes(ReduceMode mode, dp_dtype gdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,
+                        const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (mode == ReduceMode::kAccumulators) return reduce_dispatch<kFlat, 0, 2>(n, t, sp, accs, grads, gbar, sb, s);
     if (mode == ReduceMode::kGradients) {
-        if (gdt == DP_F16) return reduce_dispatch<kFlat, 1, 1>(n, t, accs, grads, gbar, sb, s);
-        return reduce_dispatch<kFlat, 1, 2>(n, t, accs, grads, gbar, sb, s);
+        if (gdt == DP_F16) return reduce_dispatch<kFlat, 1, 1>(n, t, sp, accs, grads, gbar, sb, s);
+        return reduce_dispatch<kFlat, 1, 2>(n, t, sp, accs, grads, gbar, sb, s);
     }
-    if (gdt == DP_F16) return reduce_dispatch<kFlat, 2, 1>(n, t, accs, grads, gbar, sb, s);
-    return reduce_dispatch<kFlat, 2, 2>(n, t, accs, grads, gbar, sb, s);
+    if (gdt == DP_F16) return reduce_dispatch<kFlat, 2, 1>(n, t, sp, accs, grads, gbar, sb, s);
+    return reduce_dispatch<kFlat, 2, 2>(n, t, sp, accs, grads, gbar, sb, s);
 }
 
 template <bool kFlat>
@@ -768,10 +775,10 @@ hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t
                   : accumulate_all_t<false>(gdt, first, n, t, grads, accs, s);
 }
 
-hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
-                         RoleRef gbar, StatsBuf sb, hipStream_t s) {
-    if (t.flat) return hipErrorInvalidValue;
-    return reduce_modes<false>(mode, gdt, n, t, accs, grads, gbar, sb, s);
+hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,
+                         const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t s) {
+    if (t.flat || sp.p0 < 0 || sp.p1 > t.npieces || sp.p0 > sp.p1) return hipErrorInvalidValue;
+    return reduce_modes<false>(mode, gdt, n, t, sp, accs, grads, gbar, sb, s);
 }
 
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t s) {

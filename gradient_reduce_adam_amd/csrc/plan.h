@@ -61,6 +61,7 @@ struct dp_plan {
     dpk::StatsBuf stats{nullptr, nullptr};
     dpk::FoldBuf fold{nullptr, nullptr};
     dpapi::DeviceTable full;
+    std::vector<dp_chunk> full_host;  // host copy of the [0, P) chunk table
     std::vector<dpapi::DeviceTable> ranges;
 
     // ordering state
@@ -70,6 +71,10 @@ struct dp_plan {
     bool partials_valid = false;  // piece statistics of the current g_bar exist
     int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
     bool stats_current = false;   // dp_grad_stats ran on the current g_bar
+    // a reduction issued in buckets (dp_accumulate_reduce_range): the element
+    // ranges done so far, until they cover [0, P)
+    std::vector<std::pair<int64_t, int64_t>> buckets;
+    int64_t bucket_elems = 0;
 };
 
 namespace dpapi {

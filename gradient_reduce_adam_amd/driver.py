@@ -40,6 +40,31 @@ TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
 GradProducer = Callable[[int, int, int, float], int]
 
 
+# producer(step, micro, lo, hi, stream): writes every replica's gradient of
+# elements [lo, hi) for that micro-step into its flat gradient buffer, on stream
+RangeProducer = Callable[[int, int, int, int, int], None]
+
+
+def backward_buckets(numel: Sequence[int], bucket_bytes: int, elem_bytes: int = 2) -> List[Tuple[int, int]]:
+    """Buckets for a reduction that overlaps the backward pass: runs of whole
+    tensors taken from the last tensor back to the first (the order in which
+    a backward pass finishes them), each closed once it holds at least
+    bucket_bytes of gradients.  Returned in that order."""
+    offs = [0]
+    for x in numel:
+        offs.append(offs[-1] + int(x))
+    out: List[Tuple[int, int]] = []
+    hi = offs[-1]
+    acc = 0
+    for t in range(len(numel) - 1, -1, -1):
+        acc += int(numel[t]) * elem_bytes
+        if acc >= bucket_bytes or t == 0:
+            if offs[t] < hi:
+                out.append((offs[t], hi))
+            hi, acc = offs[t], 0
+    return out
+
+
 def even_shards(P: int, shards: int) -> List[Tuple[int, int]]:
     cuts = [P * i // shards for i in range(shards + 1)]
     return [(cuts[i], cuts[i + 1]) for i in range(shards)]
@@ -147,6 +172,60 @@ class DPStep:
             s = self.read_state()
             self.scale = s["scale"]
             return s
+        return None
+
+    def step_overlapped(self, grad_slots: Sequence[int], produce: RangeProducer, buckets: Sequence[Tuple[int, int]],
+                        reduce_stream: Optional[torch.cuda.Stream] = None, sync_scale: bool = True,
+                        marks: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> Optional[dict]:
+        """One step in which the backward pass of the last micro-step hands
+        over its gradients bucket by bucket and the replica reduction follows
+        bucket by bucket (``dp_accumulate_reduce_range``); the earlier
+        micro-steps accumulate without any exchange, as a data-parallel run
+        with gradient accumulation does.
+
+        The gradient buffers are flat (grad_slots[r]: replica r's, P
+        elements), and the producer fills them range by range on this step's
+        stream.  With a separate reduce_stream, the reduction of a bucket runs
+        there as soon as the producer has written it, overlapping the
+        production of the next bucket (events order each bucket's reduction
+        after its production, and the statistics after every reduction).
+        Without one, production and reduction alternate on one stream.  Same
+        bits as ``step`` in either case.  marks, if given, are recorded on
+        this step's stream before the last micro-step and after its last
+        reduction."""
+        if self.single_pass:
+            raise ValueError("the bucketed reduction serves the two-pass update")
+        pl, h = self.plan, self.plan.handle
+        st = self.stream.cuda_stream
+        self.steps_done += 1
+        s = self.steps_done
+        for r, addr in enumerate(grad_slots):
+            dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr)
+        last = 1 if self.partials else self.a
+        for k in range(1, last):
+            produce(s, k, 0, self.P, st)
+            pl.accumulate_all(first=(k == 1), stream=st)
+        if marks is not None:
+            marks[0].record(self.stream)
+        rs = reduce_stream if reduce_stream is not None else self.stream
+        for lo, hi in buckets:
+            produce(s, last, lo, hi, st)
+            if rs is not self.stream:
+                ev = torch.cuda.Event()
+                ev.record(self.stream)
+                rs.wait_event(ev)
+            pl.accumulate_reduce_range(lo, hi, stream=rs.cuda_stream)
+        if rs is not self.stream:
+            ev = torch.cuda.Event()
+            ev.record(rs)
+            self.stream.wait_event(ev)
+        if marks is not None:
+            marks[1].record(self.stream)
+        self.finish()
+        if sync_scale:
+            state = self.read_state()
+            self.scale = state["scale"]
+            return state
         return None
 
     def read_state(self) -> dict:

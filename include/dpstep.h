@@ -229,6 +229,23 @@ dp_status dp_accumulate_all(dp_plan* plan, int32_t first, hipStream_t stream);
  * different micro-steps or before dp_state_init. */
 dp_status dp_accumulate_reduce(dp_plan* plan, hipStream_t stream);
 
+/* dp_accumulate_reduce over one bucket [begin, end) of the flat space, so the
+ * reduction can start on the gradients the backward pass has finished while
+ * it still computes the others -- the bucketed gradient all-reduce overlapped
+ * with the backward pass that the pages describe for data parallelism (first
+ * page, data-parallel all-reduce paragraph; "Data vs Tensor vs Pipeline
+ * Parallelism: When to Use Each", abhik.ai, section "What each one splits /
+ * Data parallelism").  A bucket's ends must each be a tensor start, P, or a
+ * multiple of 256 elements into their tensor (DP_ERR_INVALID_ARG otherwise).
+ * The buckets of one reduction may come in any order and on several streams;
+ * they must not overlap (DP_ERR_STATE), and together they cover [0, P).  The
+ * reduction is complete when they do: it then gives, bit for bit, the
+ * g_bar and the per-chunk statistics of dp_accumulate_reduce.  Until then
+ * dp_grad_stats, the accumulation calls and the other reductions return
+ * DP_ERR_STATE.  The caller orders dp_grad_stats after every bucket's
+ * launch, for example with events when the buckets run on other streams. */
+dp_status dp_accumulate_reduce_range(dp_plan* plan, int64_t begin, int64_t end, hipStream_t stream);
+
 /* Replica average [first page, averaging formula and reduction-order
  * paragraph]: GBAR = (sum_r SRC[r]) / n over [0, P) with a fixed pairwise order
  * (adjacent pairs by levels, an odd last term carried, binary32 partial sums),

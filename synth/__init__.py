@@ -126,6 +126,12 @@ def _gpu_lib():
                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_poke_u16.restype = ctypes.c_int
         lib.synth_poke_u16.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+        lib.synth_normal_device_multi.restype = ctypes.c_int
+        lib.synth_normal_device_multi.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p),
+                                                  ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                                  ctypes.c_int, ctypes.c_void_p]
+        lib.synth_busy_device.restype = ctypes.c_int
+        lib.synth_busy_device.argtypes = [ctypes.c_double, ctypes.c_void_p]
         _gpu = lib
     return _gpu
 
@@ -223,6 +229,49 @@ def grad_device(w, step: int, replica: int, micro: int, out_ptr: int, loss_scale
 def master_device(w, out_ptr: int, stream: int, lo: int = 0, hi: Optional[int] = None) -> None:
     hi = w.P if hi is None else hi
     device_normal(master_key(w), lo, hi - lo, scale_constant(w.master_sigma), "f32", out_ptr, stream)
+
+
+def busy_device(flops: float, stream: int) -> None:
+    """Matrix-core work of about `flops` operations on `stream`, touching no
+    memory: the compute part of a synthetic backward pass."""
+    rc = _gpu_lib().synth_busy_device(float(flops), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"synth_busy_device failed with code {rc}")
+
+
+# Backward-pass compute per parameter and token: about twice the forward's
+# 2 flops per parameter and token.
+BACKWARD_FLOPS_PER_PARAM_TOKEN = 4.0
+
+
+def grads_device_replicas(w, step: int, micro: int, slots, loss_scale: float, stream: int, lo: int = 0,
+                          hi: Optional[int] = None) -> None:
+    """``grad_device`` for every replica at once (one launch per piece of
+    [lo, hi)), into slots[r] + 2 * lo for replica r: the same values."""
+    from .workloads import grad_segments
+    hi = w.P if hi is None else hi
+    n = w.n
+    keys = (ctypes.c_uint64 * n)(*[grad_key(w, step, r, micro) for r in range(n)])
+    for start, count, c in grad_segments(w, lo, hi, loss_scale):
+        outs = (ctypes.c_void_p * n)(*[slots[r] + 2 * start for r in range(n)])
+        rc = _gpu_lib().synth_normal_device_multi(keys, outs, n, start, count, float(c), DTYPE_CODES[w.grad_dtype],
+                                                  ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"synth_normal_device_multi failed with code {rc}")
+    for r in range(n):
+        for idx, val in _injected(w, step, r, micro, lo, hi):
+            _poke_u16(slots[r] + 2 * idx, _lp_bits(val, w.grad_dtype), stream)
+
+
+def backward_bucket(w, step: int, micro: int, lo: int, hi: int, slots, loss_scale: float, stream: int,
+                    tokens: int) -> None:
+    """A synthetic backward pass over the parameters [lo, hi): the matrix-core
+    compute of one replica's backward for those parameters at `tokens` tokens
+    per micro-batch, then every replica's gradients of [lo, hi) written into
+    its slot (slots[r]: device address of replica r's gradient buffer, which
+    holds the whole flat space)."""
+    busy_device(BACKWARD_FLOPS_PER_PARAM_TOKEN * (hi - lo) * tokens, stream)
+    grads_device_replicas(w, step, micro, slots, loss_scale, stream, lo, hi)
 
 
 def _poke_u16(ptr: int, bits: int, stream: int) -> None:

@@ -72,8 +72,55 @@ __global__ void __launch_bounds__(256) gen_normal(uint64_t key, int64_t start, i
     }
 }
 
+// The same for several streams at once, one per blockIdx.y: out[y][j] is
+// position start + j of keys[y] (all with the constant c).
+constexpr int kMaxStreams = 16;
+struct MultiOut {
+    uint64_t keys[kMaxStreams];
+    void* outs[kMaxStreams];
+};
+
+template <int kDtype>
+__global__ void __launch_bounds__(256) gen_normal_multi(MultiOut m, int64_t start, int64_t count, float c) {
+    const uint64_t key = m.keys[blockIdx.y];
+    void* __restrict__ out = m.outs[blockIdx.y];
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < count; j += stride) {
+        float x = value_at(key, start + j, c);
+        if constexpr (kDtype == 0) {
+            static_cast<float*>(out)[j] = x;
+        } else if constexpr (kDtype == 1) {
+            static_cast<uint16_t*>(out)[j] = to_f16(x);
+        } else {
+            static_cast<uint16_t*>(out)[j] = to_bf16(x);
+        }
+    }
+}
+
 __global__ void poke_u16(uint16_t* p, uint32_t bits) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = static_cast<uint16_t>(bits);
+}
+
+// Stand-in for the compute of a backward pass: every wave chains `iters`
+// bf16 matrix-core products of 32x32x8 (16384 flops each) on register tiles,
+// reading and writing no memory.  The sum of the result feeds a comparison
+// that never holds, so the products are not removed.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kBusyThreads = 256;
+constexpr unsigned kBusyBlocks = 1024;
+constexpr double kFlopsPerProduct = 2.0 * 32 * 32 * 8;
+
+__global__ void __launch_bounds__(kBusyThreads) busy_mfma(int64_t iters, float* sink) {
+    const short v = static_cast<short>(threadIdx.x);
+    const s16x4 a = {v, 1, 2, 3};
+    const s16x4 b = {3, 2, 1, v};
+    f32x16 acc = {};
+    for (int64_t i = 0; i < iters; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, acc, 0, 0, 0);
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[e];
+    if (s == -1.0f && sink != nullptr) sink[0] = s;
 }
 
 }  // namespace
@@ -102,6 +149,42 @@ int synth_normal_device(uint64_t key, int64_t start, int64_t count, float c, int
         case 1: hipLaunchKernelGGL(gen_normal<1>, grid, block, 0, stream, key, start, count, c, out); break;
         default: hipLaunchKernelGGL(gen_normal<2>, grid, block, 0, stream, key, start, count, c, out); break;
     }
+    return static_cast<int>(hipGetLastError());
+}
+
+// synth_normal_device for n streams (keys[i] into outs[i], host arrays of n
+// entries, n <= 16) in one launch.
+int synth_normal_device_multi(const uint64_t* keys, const void* const* outs, int n, int64_t start, int64_t count,
+                              float c, int dtype, hipStream_t stream) {
+    if (n < 1 || n > kMaxStreams || !keys || !outs || count < 0 || dtype < 0 || dtype > 2) return -1;
+    MultiOut m{};
+    for (int i = 0; i < n; ++i) {
+        if (count > 0 && outs[i] == nullptr) return -1;
+        m.keys[i] = keys[i];
+        m.outs[i] = const_cast<void*>(outs[i]);
+    }
+    if (count == 0) return 0;
+    int64_t blocks64 = (count + 255) / 256;
+    if (blocks64 > 65536 / n) blocks64 = 65536 / n > 0 ? 65536 / n : 1;
+    dim3 grid(static_cast<unsigned>(blocks64), static_cast<unsigned>(n)), block(256);
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(gen_normal_multi<0>, grid, block, 0, stream, m, start, count, c); break;
+        case 1: hipLaunchKernelGGL(gen_normal_multi<1>, grid, block, 0, stream, m, start, count, c); break;
+        default: hipLaunchKernelGGL(gen_normal_multi<2>, grid, block, 0, stream, m, start, count, c); break;
+    }
+    return static_cast<int>(hipGetLastError());
+}
+
+// Occupies the matrix cores with about `flops` floating-point operations
+// (bf16 products, rounded up to whole products per wave) on `stream`: the
+// compute of a synthetic backward pass.  Returns 0, -1 on a bad argument, or
+// the HIP error code.
+int synth_busy_device(double flops, hipStream_t stream) {
+    if (!(flops >= 0.0)) return -1;
+    const double waves = static_cast<double>(kBusyBlocks) * (kBusyThreads / 64);
+    const int64_t iters = static_cast<int64_t>(flops / (waves * kFlopsPerProduct) + 0.999999);
+    if (iters == 0) return 0;
+    hipLaunchKernelGGL(busy_mfma, dim3(kBusyBlocks), dim3(kBusyThreads), 0, stream, iters, nullptr);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -171,17 +171,26 @@ def by_name(name: str) -> Workload:
 # segments of the flat space with their generator constants
 # ----------------------------------------------------------------------------
 def grad_segments(w: Workload, lo: int, hi: int, loss_scale: float):
-    """Yields (flat_start, count, c) pieces of [lo, hi) split at tensor
-    boundaries, with the generator constant of each piece."""
+    """Yields (flat_start, count, c) pieces of [lo, hi) with the generator
+    constant of each piece: a value depends only on its stream position and
+    its tensor's constant, so runs of tensors that share a constant are one
+    piece (one generator launch)."""
     from . import scale_constant
     off = w.offsets
     scaled = set(w.scaled_tensors)
     t = int(np.searchsorted(off, lo, side="right") - 1)
     pos = lo
+    run_start, run_c = lo, None
     while pos < hi:
         end = min(hi, int(off[t + 1]))
         if end > pos:
             mult = w.grad_multiplier if t in scaled else 1.0
-            yield pos, end - pos, scale_constant(w.grad_sigma, mult, loss_scale)
+            c = scale_constant(w.grad_sigma, mult, loss_scale)
+            if run_c is not None and c != run_c:
+                yield run_start, pos - run_start, run_c
+                run_start = pos
+            run_c = c
         pos = end
         t += 1
+    if run_c is not None and hi > run_start:
+        yield run_start, hi - run_start, run_c

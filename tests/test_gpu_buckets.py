@@ -1,0 +1,141 @@
+"""The bucketed replica reduction (dp_accumulate_reduce_range): the last
+micro-step reduced bucket by bucket, on a second stream while the producer
+writes the next bucket, in backward order or shuffled, with buckets that
+split tensors.  It must give the same bits as the whole-range reduction, and
+so agree with the oracle; the ordering rules fail loudly."""
+import numpy as np
+import pytest
+import torch
+
+import gradient_reduce_adam_amd as dp
+import synth
+from gradient_reduce_adam_amd import driver
+from synth import workloads
+
+from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = (3000, 17, 4096, 5, 70001, 256, 1, 65536, 131075)
+
+
+def _split_inside(buckets, w):
+    """Splits every bucket longer than 2048 elements once more, 256 * k
+    elements into the tensor that holds its midpoint."""
+    off = [int(x) for x in w.offsets]
+    out = []
+    for lo, hi in buckets:
+        mid = (lo + hi) // 2
+        t = max(i for i in range(w.T) if off[i] <= mid)
+        cut = off[t] + (mid - off[t]) // 256 * 256
+        if hi - lo > 2048 and lo < cut < hi:
+            out += [(cut, hi), (lo, cut)]
+        else:
+            out.append((lo, hi))
+    return out
+
+
+def _bucketed_run(w, steps, buckets, two_streams):
+    run = GpuRun(w)
+    d = run.d
+    slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
+    addrs = [t.data_ptr() for t in slots]
+
+    def produce(step, k, lo, hi, stream):
+        for r in range(w.n):
+            synth.grad_device(w, step, r, k, addrs[r] + 2 * lo, d.scale, stream, lo, hi)
+
+    rs = torch.cuda.Stream() if two_streams else None
+    try:
+        states = [d.step_overlapped(addrs, produce, buckets, reduce_stream=rs) for _ in range(steps)]
+        return run.window(0, w.P), states
+    finally:
+        run.close()
+        del slots
+
+
+def _whole_run(w, steps):
+    run = GpuRun(w)
+    try:
+        states = run.run(steps)
+        return run.window(0, w.P), states
+    finally:
+        run.close()
+
+
+def _same(a, b):
+    (wa, sa), (wb, sb) = a, b
+    for k in ("w", "m", "v", "p", "gbar"):
+        assert np.array_equal(wa[k].view(np.uint8), wb[k].view(np.uint8)), k
+    for x, y in zip(sa, sb):
+        assert np.array_equal(np.array(list(x.values()), np.float64).view(np.uint64),
+                              np.array(list(y.values()), np.float64).view(np.uint64))
+
+
+CASES = {
+    "clip_n3_a2": dict(base="gpt2_small", numel=RAGGED, n=3, a=2, max_norm=0.05, scaled_tensors=(4,), steps=3),
+    "partials_dynamic": dict(base="zero3_rank_7b", numel=RAGGED, n=4, a=1, growth_interval=2, steps=4,
+                             injections=((2, 1, 1, 70000, float("inf")),)),
+    "n1_a3": dict(base="unsharded_7b", numel=RAGGED, n=1, a=3, steps=2),
+}
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bucketed_reduction_equals_whole_bitwise(name, two_streams):
+    spec = dict(CASES[name])
+    base = workloads.by_name(spec.pop("base"))
+    steps = spec.pop("steps")
+    w = base.with_(**spec)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 64 << 10), w)
+    log(f"buckets {name} two_streams={two_streams}: {len(buckets)} buckets")
+    got = _bucketed_run(w, steps, buckets, two_streams)
+    _same(got, _whole_run(w, steps))
+    if two_streams:  # and the oracle agrees
+        ref = oracle_run(w, steps)
+        for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
+            assert_scalars_match(g, r, where=f"{name} step {s}")
+        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+
+
+def test_shuffled_buckets_equal_whole_bitwise():
+    w = workloads.gpt2_small().with_(numel=RAGGED, n=2, a=2, max_norm=0.05, scaled_tensors=(1,))
+    rng = np.random.default_rng(7)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 16 << 10), w)
+    buckets = [buckets[i] for i in rng.permutation(len(buckets))]
+    log(f"shuffled buckets: {buckets}")
+    _same(_bucketed_run(w, 2, buckets, True), _whole_run(w, 2))
+
+
+def test_bucket_ordering_errors():
+    w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=1, scaled_tensors=())
+    run = GpuRun(w)
+    d, pl, s = run.d, run.d.plan, run.stream
+    try:
+        for r in range(w.n):
+            run.slots[r].zero_()
+            pl.bind("grad", run.slots[r], r)
+        for lo, hi in ((3, 5000), (0, 4999), (100, 300)):  # ends off the piece grid
+            with pytest.raises(dp.DpError) as e:
+                pl.accumulate_reduce_range(lo, hi, stream=s)
+            assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            pl.accumulate_reduce_range(0, w.P + 1, stream=s)
+        assert e.value.status == dp.DP_ERR_RANGE
+        pl.accumulate_reduce_range(5000, 8000, stream=s)  # a tensor
+        with pytest.raises(dp.DpError) as e:  # overlaps it
+            pl.accumulate_reduce_range(5256, 8700, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        for call in (lambda: pl.grad_stats(False, 0.0, stream=s), lambda: pl.accumulate_all(True, stream=s),
+                     lambda: pl.accumulate_reduce(stream=s)):
+            with pytest.raises(dp.DpError) as e:  # the reduction is half done
+                call()
+            assert e.value.status == dp.DP_ERR_STATE and "bucketed" in e.value.message
+        pl.accumulate_reduce_range(256, 5000, stream=s)  # 256 elements into tensor 0
+        pl.accumulate_reduce_range(8000, 8700, stream=s)
+        pl.accumulate_reduce_range(0, 256, stream=s)  # complete now
+        pl.grad_stats(False, 0.0, stream=s)
+        pl.adam_step(w.lr, w.eps, w.weight_decay, stream=s)
+        assert pl.read_state(stream=s)["t"] == 1
+    finally:
+        run.close()

@@ -35,6 +35,22 @@ def test_generator_device_twin_bit_identical(dtype):
         assert got.tobytes() == host.tobytes()
 
 
+def test_generator_all_replicas_launch_equals_per_replica():
+    """The one-launch generator of every replica's gradient (used by the
+    synthetic backward pass) writes the same values as the per-replica one,
+    injected non-finite values included."""
+    w = workloads.gpt2_small().with_(numel=(3000, 17, 4096, 70001), n=5, a=2, scaled_tensors=(1, 3),
+                                     injections=((1, 2, 2, 4000, float("inf")),))
+    s = torch.cuda.current_stream().cuda_stream
+    multi = torch.zeros((w.n, w.P), dtype=torch.int16, device="cuda")
+    single = torch.zeros((w.n, w.P), dtype=torch.int16, device="cuda")
+    lo, hi = 2000, w.P - 5
+    synth.grads_device_replicas(w, 1, 2, [multi[r].data_ptr() for r in range(w.n)], 4.0, s, lo, hi)
+    for r in range(w.n):
+        synth.grad_device(w, 1, r, 2, single[r].data_ptr() + 2 * lo, 4.0, s, lo, hi)
+    assert torch.equal(multi, single)
+
+
 # ----------------------------------------------------------------------------
 # accumulation and reduction are bit-exact
 # ----------------------------------------------------------------------------
