@@ -50,6 +50,9 @@ def parse():
                     help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
                          "update in one read of the state (runs without clipping); auto: single-pass when the "
                          "workload does not clip")
+    ap.add_argument("--state", choices=("hbm", "host"), default="hbm",
+                    help="where master, m and v live: HBM, or pinned host memory that the update kernels read and "
+                         "write across PCIe (the offload variant)")
     ap.add_argument("--checkpoint-dir", default="", metavar="DIR",
                     help="after the timed steps, save the state to DIR as 8 shards and restore it as 4, and print "
                          "a second JSON line with the save and restore rates")
@@ -201,8 +204,11 @@ def measure_checkpoint(d, directory: str) -> dict:
             "save_gbps": state_bytes / t_save / 1e9, "load_gbps": state_bytes / t_load / 1e9, "unit": "GB/s"}
 
 
+PEAK_PCIE_GBPS = 2 * 63.0  # PCIe 5.0 x16, both directions (32 GT/s, 128b/130b)
+
+
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
-            ckpt_dir: str = ""):
+            ckpt_dir: str = "", state: str = "hbm"):
     import torch
 
     import synth
@@ -219,7 +225,8 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
-                      growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single)
+                      growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single,
+                      state_location=state)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -452,7 +459,7 @@ def main():
         return
     single = single_pass_for(w, args.update)
     elapsed, per_kind, state, ckpt = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
-                                             args.bind, single, args.checkpoint_dir)
+                                             args.bind, single, args.checkpoint_dir, args.state)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
@@ -502,6 +509,17 @@ def main():
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
         "cpu_baseline": None,
     }
+    if args.state == "host":
+        # the offload variant: the update is bound by PCIe, which carries the
+        # state both ways (12 B/param read, 12 B/param written)
+        upd = "reduce_adamw" if single else "adamw"
+        upd_ms = per_kind[upd]["avg_ms"]
+        line["metric"] = "params updated/sec per full DP step, optimizer state in pinned host memory"
+        line["config"]["state_location"] = "host (pinned, read and written by the update kernels over PCIe)"
+        line["roofline"] = {"kernel": upd, "bound": "pcie", "achieved": 24.0 * w.P / (upd_ms * 1e-3) / 1e9,
+                            "peak": PEAK_PCIE_GBPS, "unit": "GB/s",
+                            "frac": 24.0 * w.P / (upd_ms * 1e-3) / 1e9 / PEAK_PCIE_GBPS, "traffic": None,
+                            "bytes_per_launch": 24.0 * w.P, "avg_launch_ms": upd_ms}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(line), flush=True)

@@ -21,7 +21,7 @@ once.
 
 HBM layout (flat parameter space of P elements, tensors in list order):
 master, exp_avg, exp_avg_sq: binary32 [P] (two banks of each with
-``single_pass``); param: bf16/fp16 [P]; acc[r]: binary32 [P] per replica
+``single_pass``; in pinned host memory with ``state_location="host"``); param: bf16/fp16 [P]; acc[r]: binary32 [P] per replica
 (absent for partials; with n = 1, acc[0] is also g_bar); gbar: binary32 [P]
 when n > 1 or with partials, and not with ``single_pass``; gradients: the
 producer's buffers, bound per call.
@@ -77,7 +77,7 @@ class DPStep:
                  backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, partials: bool = False,
                  shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
                  device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True,
-                 single_pass: bool = False):
+                 single_pass: bool = False, state_location: str = "hbm"):
         if partials and a != 1:
             raise ValueError("incoming partials are reduced directly: a must be 1")
         if single_pass and max_norm > 0.0:
@@ -86,7 +86,10 @@ class DPStep:
             raise ValueError("the single pass reads every replica's last micro-step at once: it needs fused = True")
         if single_pass and shards is not None and list(shards) != [(0, sum(numel))]:
             raise ValueError("the single pass updates the whole range in one call")
+        if state_location not in ("hbm", "host"):
+            raise ValueError("state_location is 'hbm' or 'host'")
         self.n, self.a, self.partials, self.fused, self.single_pass = n, a, partials, fused, single_pass
+        self.state_location = state_location
         self.lr, self.eps, self.weight_decay, self.max_norm = lr, eps, weight_decay, max_norm
         self.scaler = scaler
         self.plan = Plan(numel, n, grad_dtype, param_dtype, chunk_elems)
@@ -94,9 +97,12 @@ class DPStep:
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         f32 = dict(dtype=torch.float32, device=self.device)
-        self.master = torch.zeros(P, **f32)
-        self.exp_avg = torch.zeros(P, **f32)
-        self.exp_avg_sq = torch.zeros(P, **f32)
+        # optimizer state (master, m, v): in HBM, or offloaded to pinned host
+        # memory that the update kernels read and write across PCIe
+        st32 = f32 if state_location == "hbm" else dict(dtype=torch.float32, pin_memory=True)
+        self.master = torch.zeros(P, **st32)
+        self.exp_avg = torch.zeros(P, **st32)
+        self.exp_avg_sq = torch.zeros(P, **st32)
         self.param = torch.zeros(P, dtype=TORCH_DTYPES[param_dtype], device=self.device)
         self.acc: List[torch.Tensor] = [] if partials else [torch.zeros(P, **f32) for _ in range(n)]
         if n == 1 and not partials:
@@ -106,7 +112,7 @@ class DPStep:
         # state banks: (master, exp_avg, exp_avg_sq); bank 1 only for the single pass
         self.banks = [(self.master, self.exp_avg, self.exp_avg_sq)]
         if single_pass:
-            self.banks.append(tuple(torch.zeros(P, **f32) for _ in range(3)))
+            self.banks.append(tuple(torch.zeros(P, **st32) for _ in range(3)))
         pl = self.plan
         for b, (w_, m_, v_) in enumerate(self.banks):
             pl.bind("master", w_, b)
@@ -126,11 +132,17 @@ class DPStep:
 
     # -- setup ------------------------------------------------------------
     def set_master(self, fill: Callable[[int], None]) -> None:
-        """fill(address) writes the initial binary32 master weights; the
-        low-precision copy starts as their round-to-nearest-even image."""
-        fill(self.master.data_ptr())
+        """fill(address) writes the initial binary32 master weights into device
+        memory; the low-precision copy starts as their round-to-nearest-even
+        image."""
+        dev = self.master if self.state_location == "hbm" else torch.empty(self.P, dtype=torch.float32,
+                                                                            device=self.device)
+        fill(dev.data_ptr())
         torch.cuda.current_stream(self.device).wait_stream(self.stream)
-        self.param.copy_(self.master.to(self.param.dtype))
+        self.param.copy_(dev.to(self.param.dtype))
+        if dev is not self.master:
+            self.master.copy_(dev)
+            torch.cuda.synchronize(self.device)
 
     # -- one step ---------------------------------------------------------
     def issue_gradients(self, produce: GradProducer, step: int) -> None:
