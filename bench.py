@@ -50,6 +50,9 @@ def parse():
                     help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
                          "update in one read of the state (runs without clipping); auto: single-pass when the "
                          "workload does not clip")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured into a HIP graph (the per-kernel times still come from "
+                         "an eager timed run)")
     ap.add_argument("--state", choices=("hbm", "host"), default="hbm",
                     help="where master, m and v live: HBM, or pinned host memory that the update kernels read and "
                          "write across PCIe (the offload variant)")
@@ -208,7 +211,7 @@ PEAK_PCIE_GBPS = 2 * 63.0  # PCIe 5.0 x16, both directions (32 GT/s, 128b/130b)
 
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
-            ckpt_dir: str = "", state: str = "hbm"):
+            ckpt_dir: str = "", state: str = "hbm", graph: bool = False):
     import torch
 
     import synth
@@ -226,7 +229,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                       growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single,
-                      state_location=state)
+                      state_location=state, stream=torch.cuda.Stream() if graph else None)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -303,6 +306,18 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         one_step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if graph:  # the same step as one HIP graph: capture, warm up, time the replays
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st_obj):
+            one_step(False)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     state = d.read_state()
     ckpt = measure_checkpoint(d, ckpt_dir) if ckpt_dir else None
     per_kind = {}
@@ -459,7 +474,7 @@ def main():
         return
     single = single_pass_for(w, args.update)
     elapsed, per_kind, state, ckpt = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
-                                             args.bind, single, args.checkpoint_dir, args.state)
+                                             args.bind, single, args.checkpoint_dir, args.state, args.graph)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
@@ -496,7 +511,8 @@ def main():
                    "update_arithmetic": "f64", "clip": w.max_norm, "loss_scale": w.scaler,
                    "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)",
                    "chunk_elems": args.chunk or 16384, "binding": args.bind,
-                   "update": "single-pass" if single else "two-pass"},
+                   "update": "single-pass" if single else "two-pass",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "hbm_gbps": hbm_gbps,
         "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
         "bytes_per_param_step": sum(per_param.values()),

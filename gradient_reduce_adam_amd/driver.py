@@ -240,6 +240,37 @@ class DPStep:
             return state
         return None
 
+    def issue_fixed(self, grad_slots: Sequence[Sequence[int]]) -> None:
+        """One whole step (accumulation, reduction, statistics, update) that
+        reads micro-step k's gradient of replica r from grad_slots[k - 1][r],
+        with no host synchronisation: the form a graph can capture."""
+        pl, st, h = self.plan, self.stream.cuda_stream, self.plan.handle
+        last = 1 if self.partials else self.a
+        if not (self.partials or self.fused):
+            raise ValueError("the fixed-buffer step uses the fused sequence")
+        for k in range(1, last):
+            for r in range(self.n):
+                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, grad_slots[k - 1][r])
+            pl.accumulate_all(first=(k == 1), stream=st)
+        for r in range(self.n):
+            dp_plan_bind_flat(h, DP_ROLE_GRAD, r, grad_slots[last - 1][r])
+        if not self.single_pass:
+            pl.accumulate_reduce(stream=st)
+        self.finish()
+
+    def capture_step(self, grad_slots: Sequence[Sequence[int]]) -> "torch.cuda.CUDAGraph":
+        """Captures ``issue_fixed`` into a HIP graph on this step's stream
+        (which must not be the null stream).  Each replay runs one more step on
+        whatever the gradient buffers then hold; the plan's host-side call
+        checks ran once, at capture.  The step's launches are kernels only (no
+        memset nodes)."""
+        if self.stream.cuda_stream == 0:
+            raise ValueError("capture needs a non-default stream: pass stream=torch.cuda.Stream()")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            self.issue_fixed(grad_slots)
+        return g
+
     def read_state(self) -> dict:
         return self.plan.read_state(stream=self.stream.cuda_stream)
 
