@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--state", choices=("hbm", "host"), default="hbm",
                     help="where master, m and v live: HBM, or pinned host memory that the update kernels read and "
                          "write across PCIe (the offload variant)")
+    ap.add_argument("--offload", choices=("direct", "staged"), default="direct",
+                    help="with --state host: the kernels access the host state directly, or it is copied through "
+                         "device slots on two copy streams (two-pass update only)")
     ap.add_argument("--checkpoint-dir", default="", metavar="DIR",
                     help="after the timed steps, save the state to DIR as 8 shards and restore it as 4, and print "
                          "a second JSON line with the save and restore rates")
@@ -210,8 +213,37 @@ def measure_checkpoint(d, directory: str) -> dict:
 PEAK_PCIE_GBPS = 2 * 63.0  # PCIe 5.0 x16, both directions (32 GT/s, 128b/130b)
 
 
+def measure_pcie_copies(nbytes: int = 1 << 30, reps: int = 5) -> dict:
+    """Plain copies between pinned host memory and HBM, one direction at a
+    time and both at once on two streams: the practical PCIe ceiling the
+    offloaded update is held to."""
+    import torch
+
+    h_in = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    h_out = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d_in = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d_out = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def run(h2d: bool, d2h: bool) -> float:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            if h2d:
+                with torch.cuda.stream(s1):
+                    d_in.copy_(h_in, non_blocking=True)
+            if d2h:
+                with torch.cuda.stream(s2):
+                    h_out.copy_(d_out, non_blocking=True)
+        torch.cuda.synchronize()
+        return (int(h2d) + int(d2h)) * nbytes * reps / (time.perf_counter() - t0) / 1e9
+
+    run(True, True)
+    return {"h2d_gbps": run(True, False), "d2h_gbps": run(False, True), "both_gbps": run(True, True)}
+
+
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
-            ckpt_dir: str = "", state: str = "hbm", graph: bool = False):
+            ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct"):
     import torch
 
     import synth
@@ -229,7 +261,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                       growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single,
-                      state_location=state, stream=torch.cuda.Stream() if graph else None)
+                      state_location=state, stream=torch.cuda.Stream() if graph else None, offload=offload)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -296,7 +328,10 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
             return
         timed("accumulate_reduce", lambda: plan.accumulate_reduce(stream=stream), rec)
         timed("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream), rec)
-        timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
+        if d.offload == "staged":
+            timed("adamw", d.staged_update, rec)
+        else:
+            timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
 
     for _ in range(warmup):
         one_step(False)
@@ -474,7 +509,8 @@ def main():
         return
     single = single_pass_for(w, args.update)
     elapsed, per_kind, state, ckpt = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
-                                             args.bind, single, args.checkpoint_dir, args.state, args.graph)
+                                             args.bind, single, args.checkpoint_dir, args.state, args.graph,
+                                             args.offload)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
@@ -531,7 +567,10 @@ def main():
         upd = "reduce_adamw" if single else "adamw"
         upd_ms = per_kind[upd]["avg_ms"]
         line["metric"] = "params updated/sec per full DP step, optimizer state in pinned host memory"
-        line["config"]["state_location"] = "host (pinned, read and written by the update kernels over PCIe)"
+        line["config"]["state_location"] = ("host (pinned, read and written by the update kernels over PCIe)"
+                                            if args.offload == "direct" else
+                                            "host (pinned, copied through device slots on two copy streams)")
+        line["pcie_copies"] = measure_pcie_copies()
         line["roofline"] = {"kernel": upd, "bound": "pcie", "achieved": 24.0 * w.P / (upd_ms * 1e-3) / 1e9,
                             "peak": PEAK_PCIE_GBPS, "unit": "GB/s",
                             "frac": 24.0 * w.P / (upd_ms * 1e-3) / 1e9 / PEAK_PCIE_GBPS, "traffic": None,

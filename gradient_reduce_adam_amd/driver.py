@@ -32,7 +32,7 @@ from typing import Callable, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import DP_ROLE_GRAD, Plan, dp_plan_bind_flat
+from . import DP_ROLE_EXP_AVG, DP_ROLE_EXP_AVG_SQ, DP_ROLE_GRAD, DP_ROLE_MASTER, Plan, dp_plan_bind_flat
 
 TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -77,7 +77,8 @@ class DPStep:
                  backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, partials: bool = False,
                  shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
                  device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True,
-                 single_pass: bool = False, state_location: str = "hbm"):
+                 single_pass: bool = False, state_location: str = "hbm", offload: str = "direct",
+                 stage_elems: int = 1 << 24):
         if partials and a != 1:
             raise ValueError("incoming partials are reduced directly: a must be 1")
         if single_pass and max_norm > 0.0:
@@ -88,6 +89,11 @@ class DPStep:
             raise ValueError("the single pass updates the whole range in one call")
         if state_location not in ("hbm", "host"):
             raise ValueError("state_location is 'hbm' or 'host'")
+        if offload not in ("direct", "staged"):
+            raise ValueError("offload is 'direct' or 'staged'")
+        if offload == "staged" and (state_location != "host" or single_pass):
+            raise ValueError("the staged offload moves a host-resident state for the two-pass update")
+        self.offload = offload
         self.n, self.a, self.partials, self.fused, self.single_pass = n, a, partials, fused, single_pass
         self.state_location = state_location
         self.lr, self.eps, self.weight_decay, self.max_norm = lr, eps, weight_decay, max_norm
@@ -126,6 +132,16 @@ class DPStep:
         self.shards = list(shards) if shards is not None else [(0, P)]
         for b, e in self.shards:
             pl.prepare_range(b, e)
+        if offload == "staged":
+            # three device slots of stage_elems elements of master, m, v, and
+            # the pieces of every shard that pass through them
+            self.stage_elems = int(stage_elems)
+            self.stage = [tuple(torch.empty(self.stage_elems, **f32) for _ in range(3)) for _ in range(3)]
+            self.stage_pieces = [(lo, min(e, lo + self.stage_elems)) for b, e in self.shards
+                                 for lo in range(b, e, self.stage_elems)]
+            for lo, hi in self.stage_pieces:
+                pl.prepare_range(lo, hi)
+            self.copy_in, self.copy_out = torch.cuda.Stream(self.device), torch.cuda.Stream(self.device)
         pl.state_init(beta1, beta2, scaler, init_scale, backoff, growth, growth_interval, stream=self.stream)
         self.scale = 1.0 if scaler == "none" else float(init_scale)
         self.steps_done = 0
@@ -173,8 +189,52 @@ class DPStep:
             pl.reduce_adam_step(self.lr, self.eps, self.weight_decay, stream=st)
             return
         pl.grad_stats(scan=False, max_norm=self.max_norm, stream=st)
+        if self.offload == "staged":
+            self.staged_update()
+            return
         for b, e in self.shards:
             pl.adam_step(self.lr, self.eps, self.weight_decay, b, e, stream=st)
+
+    def staged_update(self) -> None:
+        """The update with the state streamed through device slots: piece j's
+        master, m and v are copied in on one stream, updated in slot j mod 3
+        (the roles rebound to the slot) on the step's stream, and copied back
+        on a third; the copies of neighbouring pieces overlap the update."""
+        pl, h, st = self.plan, self.plan.handle, self.stream
+        host = (self.master, self.exp_avg, self.exp_avg_sq)
+        roles = (DP_ROLE_MASTER, DP_ROLE_EXP_AVG, DP_ROLE_EXP_AVG_SQ)
+        slot_free = [None, None, None]  # event: the slot's last copy-out finished
+        done = []
+        # every copy-in comes after the work already on the step's stream, which
+        # includes the previous step's copy-outs
+        self.copy_in.wait_stream(st)
+        for j, (lo, hi) in enumerate(self.stage_pieces):
+            k, n = j % 3, hi - lo
+            slot = self.stage[k]
+            if slot_free[k] is not None:
+                self.copy_in.wait_event(slot_free[k])
+            with torch.cuda.stream(self.copy_in):
+                for d_, h_ in zip(slot, host):
+                    d_[:n].copy_(h_[lo:hi], non_blocking=True)
+            ready = torch.cuda.Event()
+            ready.record(self.copy_in)
+            st.wait_event(ready)
+            for role, d_ in zip(roles, slot):
+                dp_plan_bind_flat(h, role, 0, d_.data_ptr() - 4 * lo)
+            pl.adam_step(self.lr, self.eps, self.weight_decay, lo, hi, stream=st.cuda_stream)
+            updated = torch.cuda.Event()
+            updated.record(st)
+            self.copy_out.wait_event(updated)
+            with torch.cuda.stream(self.copy_out):
+                for d_, h_ in zip(slot, host):
+                    h_[lo:hi].copy_(d_[:n], non_blocking=True)
+            slot_free[k] = torch.cuda.Event()
+            slot_free[k].record(self.copy_out)
+            done.append(slot_free[k])
+        for ev in done[-3:]:
+            st.wait_event(ev)
+        for role, t in zip(roles, host):  # the bindings point at the host state again
+            dp_plan_bind_flat(h, role, 0, t.data_ptr())
 
     def step(self, produce: GradProducer, sync_scale: bool = True) -> Optional[dict]:
         self.steps_done += 1

@@ -39,14 +39,14 @@ class GpuRun:
     """A workload on the GPU: the library's driver plus device-generated inputs."""
 
     def __init__(self, w, shards=None, chunk_elems: int = 0, fused: bool = True, single_pass: bool = False,
-                 state_location: str = "hbm", stream=None):
+                 state_location: str = "hbm", stream=None, **extra):
         self.w = w
         self.d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                                weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                                scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                                growth_interval=w.growth_interval, partials=w.partials, shards=shards,
                                chunk_elems=chunk_elems, fused=fused, single_pass=single_pass,
-                               state_location=state_location, stream=stream)
+                               state_location=state_location, stream=stream, **extra)
         slots = w.n if (w.partials or fused) else 1  # the fused step holds every replica's gradient at once
         self.slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(slots)]
         self.stream = self.d.stream.cuda_stream
