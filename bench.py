@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph (the per-kernel times still come from "
                          "an eager timed run)")
+    ap.add_argument("--layout", choices=("auto", "packed", "spread"), default="auto",
+                    help="HBM placement of the update's arrays (see driver.DPStep)")
     ap.add_argument("--state", choices=("hbm", "host"), default="hbm",
                     help="where master, m and v live: HBM, or pinned host memory that the update kernels read and "
                          "write across PCIe (the offload variant)")
@@ -243,7 +245,8 @@ def measure_pcie_copies(nbytes: int = 1 << 30, reps: int = 5) -> dict:
 
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
-            ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct"):
+            ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct",
+            layout: str = "auto"):
     import torch
 
     import synth
@@ -261,7 +264,8 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
                       growth_interval=w.growth_interval, partials=w.partials, chunk_elems=chunk, single_pass=single,
-                      state_location=state, stream=torch.cuda.Stream() if graph else None, offload=offload)
+                      state_location=state, stream=torch.cuda.Stream() if graph else None, offload=offload,
+                      layout=layout)
     st_obj = d.stream
     stream = st_obj.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, stream))
@@ -290,7 +294,8 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     budget = min(RESIDENT_GRAD_BUDGET, free - 4e9)  # leave room for the library's tables and torch
     nbuf = len(calls) if len(calls) * per_buf <= budget else int(budget // per_buf)
     nbuf = max(nbuf, 2 * w.n if not w.partials else w.n)
-    bufs = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(nbuf)]
+    # one allocation; a micro-step's n replicas take consecutive rows
+    bufs = list(torch.empty((nbuf, w.P), dtype=torch.int16, device="cuda").unbind(0))
     addr = {}
     for i, (r, k) in enumerate(calls):
         b = bufs[i % nbuf]
@@ -359,10 +364,11 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     for kind, pairs in events.items():
         ms = [a.elapsed_time(b) for a, b in pairs]
         per_kind[kind] = {"launches": len(ms), "avg_ms": sum(ms) / len(ms), "total_ms": sum(ms)}
+    used_layout = d.layout
     d.close()
     del bufs
     torch.cuda.empty_cache()
-    return elapsed, per_kind, state, ckpt
+    return elapsed, per_kind, state, ckpt, used_layout
 
 
 def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
@@ -508,9 +514,9 @@ def main():
             print(json.dumps(line), flush=True)
         return
     single = single_pass_for(w, args.update)
-    elapsed, per_kind, state, ckpt = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
-                                             args.bind, single, args.checkpoint_dir, args.state, args.graph,
-                                             args.offload)
+    elapsed, per_kind, state, ckpt, layout = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
+                                                     args.bind, single, args.checkpoint_dir, args.state, args.graph,
+                                                     args.offload, args.layout)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
@@ -548,7 +554,7 @@ def main():
                    "global_batch": 4 * w.n * w.a, "parallelism": "dp (replicas in one GPU's HBM)",
                    "chunk_elems": args.chunk or 16384, "binding": args.bind,
                    "update": "single-pass" if single else "two-pass",
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager", "layout": layout},
         "hbm_gbps": hbm_gbps,
         "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
         "bytes_per_param_step": sum(per_param.values()),

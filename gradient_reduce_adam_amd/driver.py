@@ -19,7 +19,8 @@ Gradients come from a caller-supplied producer, standing in for the backward
 pass; the fused sequence needs the n replicas' gradients of one micro-step at
 once.
 
-HBM layout (flat parameter space of P elements, tensors in list order):
+HBM layout (flat parameter space of P elements, tensors in list order; see
+``layout`` for where the arrays sit relative to each other):
 master, exp_avg, exp_avg_sq: binary32 [P] (two banks of each with
 ``single_pass``; in pinned host memory with ``state_location="host"``); param: bf16/fp16 [P]; acc[r]: binary32 [P] per replica
 (absent for partials; with n = 1, acc[0] is also g_bar); gbar: binary32 [P]
@@ -78,7 +79,7 @@ class DPStep:
                  shards: Optional[Sequence[Tuple[int, int]]] = None, chunk_elems: int = 0,
                  device: str = "cuda:0", stream: Optional[torch.cuda.Stream] = None, fused: bool = True,
                  single_pass: bool = False, state_location: str = "hbm", offload: str = "direct",
-                 stage_elems: int = 1 << 24):
+                 stage_elems: int = 1 << 24, layout: str = "auto"):
         if partials and a != 1:
             raise ValueError("incoming partials are reduced directly: a must be 1")
         if single_pass and max_norm > 0.0:
@@ -103,22 +104,38 @@ class DPStep:
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         f32 = dict(dtype=torch.float32, device=self.device)
-        # optimizer state (master, m, v): in HBM, or offloaded to pinned host
-        # memory that the update kernels read and write across PCIe
-        st32 = f32 if state_location == "hbm" else dict(dtype=torch.float32, pin_memory=True)
-        self.master = torch.zeros(P, **st32)
-        self.exp_avg = torch.zeros(P, **st32)
-        self.exp_avg_sq = torch.zeros(P, **st32)
-        self.param = torch.zeros(P, dtype=TORCH_DTYPES[param_dtype], device=self.device)
-        self.acc: List[torch.Tensor] = [] if partials else [torch.zeros(P, **f32) for _ in range(n)]
+        pdt = TORCH_DTYPES[param_dtype]
+        own_gbar = not (n == 1 and not partials) and not single_pass
+        nbanks = 2 if single_pass else 1
+        # The arrays one update streams together: g_bar (two passes), master, m
+        # and v of every bank, and the parameters.
+        update = ([("gbar", torch.float32)] if own_gbar else []) + \
+            [(f"{r}{b}", torch.float32) for b in range(nbanks) for r in ("master", "exp_avg", "exp_avg_sq")] + \
+            [("param", pdt)]
+        self.layout = self._choose_layout(layout, state_location, update, P, 0 if partials else n)
+        arrays = {}
+        if self.layout == "spread":
+            arrays = self._spread_arrays(update, P, 0 if partials else n)
+        else:
+            # optimizer state (master, m, v): in HBM, or offloaded to pinned
+            # host memory that the update kernels read and write across PCIe
+            st32 = f32 if state_location == "hbm" else dict(dtype=torch.float32, pin_memory=True)
+            for name, dt in update:
+                host = name.startswith(("master", "exp_avg")) and state_location == "host"
+                arrays[name] = torch.zeros(P, **(st32 if host else dict(dtype=dt, device=self.device)))
+            # the n accumulators are rows of one allocation: the micro-step
+            # launch over all replicas then streams one contiguous region
+            if not partials:
+                arrays["acc"] = torch.zeros((n, P), **f32)
+        self.master, self.exp_avg, self.exp_avg_sq = arrays["master0"], arrays["exp_avg0"], arrays["exp_avg_sq0"]
+        self.param = arrays["param"]
+        self.acc: List[torch.Tensor] = list(arrays["acc"].unbind(0)) if not partials else []
         if n == 1 and not partials:
             self.gbar = self.acc[0]
         else:
-            self.gbar = None if single_pass else torch.zeros(P, **f32)
+            self.gbar = arrays.get("gbar")
         # state banks: (master, exp_avg, exp_avg_sq); bank 1 only for the single pass
-        self.banks = [(self.master, self.exp_avg, self.exp_avg_sq)]
-        if single_pass:
-            self.banks.append(tuple(torch.zeros(P, **st32) for _ in range(3)))
+        self.banks = [tuple(arrays[f"{r}{b}"] for r in ("master", "exp_avg", "exp_avg_sq")) for b in range(nbanks)]
         pl = self.plan
         for b, (w_, m_, v_) in enumerate(self.banks):
             pl.bind("master", w_, b)
@@ -145,6 +162,48 @@ class DPStep:
         pl.state_init(beta1, beta2, scaler, init_scale, backoff, growth, growth_interval, stream=self.stream)
         self.scale = 1.0 if scaler == "none" else float(init_scale)
         self.steps_done = 0
+
+    # -- HBM layout ---------------------------------------------------------
+    # Where the arrays of one kernel sit relative to each other changes its
+    # bandwidth on MI355X by up to 8%, and not by a rule that held across the
+    # workloads measured (16 GiB slot offsets sped up the update of some and
+    # slowed others).  "packed" (the default, also what "auto" picks) lets
+    # torch place each array; "spread" carves the update's arrays from one
+    # allocation at slot offsets that are multiples of 16 GiB, with the
+    # accumulators after them, holding the gaps between slots allocated too.
+    SLOT = 16 << 30
+    ALIGN = 2 << 20
+
+    def _spread_plan(self, update, P: int, nacc: int):
+        nbytes = [P * torch.tensor([], dtype=dt).element_size() for _, dt in update]
+        slot = self.SLOT * max(1, -(-max(nbytes) // self.SLOT))
+        offs = [k * slot for k in range(len(update))]
+        acc_off = -(-(offs[-1] + nbytes[-1]) // self.ALIGN) * self.ALIGN
+        total = acc_off + nacc * P * 4
+        return slot, offs, nbytes, acc_off, total
+
+    def _choose_layout(self, layout: str, state_location: str, update, P: int, nacc: int) -> str:
+        if layout not in ("auto", "packed", "spread"):
+            raise ValueError("layout is 'auto', 'packed' or 'spread'")
+        if layout == "packed" or state_location != "hbm" or P == 0:
+            return "packed"
+        if layout == "spread":
+            total = self._spread_plan(update, P, nacc)[-1]
+            free, _ = torch.cuda.mem_get_info(self.device)
+            if total > free:
+                raise MemoryError(f"the spread layout needs {total} bytes of HBM, {free} are free")
+            return "spread"
+        return "packed"
+
+    def _spread_arrays(self, update, P: int, nacc: int) -> dict:
+        slot, offs, nbytes, acc_off, total = self._spread_plan(update, P, nacc)
+        self.arena = torch.empty(total, dtype=torch.uint8, device=self.device)
+        out = {}
+        for (name, dt), off, nb in zip(update, offs, nbytes):
+            out[name] = self.arena[off:off + nb].view(dt).zero_()
+        if nacc:
+            out["acc"] = self.arena[acc_off:acc_off + nacc * P * 4].view(torch.float32).view(nacc, P).zero_()
+        return out
 
     # -- setup ------------------------------------------------------------
     def set_master(self, fill: Callable[[int], None]) -> None:

@@ -275,6 +275,25 @@ def test_single_pass_skip_leaves_state_and_params_unchanged():
         run.close()
 
 
+@pytest.mark.parametrize("single", [False, True])
+def test_spread_layout_equals_packed_bitwise(single):
+    """Where the arrays sit in HBM changes nothing but speed."""
+    w = workloads.tiny().with_(numel=RAGGED, n=3, a=2, steps=3)
+    outs = []
+    for layout in ("packed", "spread"):
+        run = GpuRun(w, single_pass=single, layout=layout)
+        try:
+            assert run.d.layout == layout
+            st = run.run(3)
+            outs.append((run.window(0, w.P), st))
+        finally:
+            run.close()
+    (a, sa), (b, sb) = outs
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    assert [x["t"] for x in sa] == [x["t"] for x in sb]
+
+
 def test_sharded_update_equals_unsharded_bitwise():
     """Sharding changes the layout, not the update: eight uneven ranges give
     the same bits as one call on the whole range."""
