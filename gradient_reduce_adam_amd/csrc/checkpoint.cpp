@@ -618,15 +618,17 @@ dp_status alloc_pinned(Pinned* b) {
     return DP_OK;
 }
 
-// Copies elements [lo, hi) of a role between device and host, one copy per
-// contiguous device segment (one for a flat binding, one per tensor piece for
-// per-tensor bindings).  to_host selects the direction.
+// Copies elements [lo, hi) of a role between its memory and a host buffer,
+// one copy per contiguous segment (one for a flat binding, one per tensor
+// piece for per-tensor bindings).  to_host selects the direction.  The role's
+// memory may be device memory or pinned host memory (an offloaded state): the
+// runtime tells them apart by address.
 dp_status copy_role(const dp_plan* p, const dpapi::Binding& b, size_t es, int64_t lo, int64_t hi, void* host,
                     bool to_host, hipStream_t stream) {
     char* h = static_cast<char*>(host);
-    auto one = [&](char* dev, size_t bytes, char* hp) {
-        return to_host ? hipMemcpyAsync(hp, dev, bytes, hipMemcpyDeviceToHost, stream)
-                       : hipMemcpyAsync(dev, hp, bytes, hipMemcpyHostToDevice, stream);
+    auto one = [&](char* mem, size_t bytes, char* hp) {
+        return to_host ? hipMemcpyAsync(hp, mem, bytes, hipMemcpyDefault, stream)
+                       : hipMemcpyAsync(mem, hp, bytes, hipMemcpyDefault, stream);
     };
     hipError_t e = hipSuccess;
     if (b.flat) {

@@ -172,3 +172,31 @@ def test_load_errors(tmp_path):
         assert e.value.status == dp.DP_ERR_STATE and "optimizer settings" in e.value.message
     finally:
         run.close()
+
+
+def test_offloaded_state_round_trip(tmp_path):
+    """A run whose state lives in pinned host memory saves a checkpoint that
+    an HBM-resident run restores, and both finish with the same bits as an
+    uninterrupted run."""
+    w = workloads.tiny().with_(numel=RAGGED, n=2, a=2, steps=4)
+    P = w.P
+    run = GpuRun(w)
+    try:
+        run.run(4)
+        whole = _snapshot(run)
+    finally:
+        run.close()
+    run = GpuRun(w, state_location="host")
+    try:
+        run.run(2)
+        run.d.save_checkpoint(str(tmp_path), 2, ranges=_ranges(P, 3))
+    finally:
+        run.close()
+    run = GpuRun(w)
+    try:
+        run.d.load_checkpoint(str(tmp_path), ranges=_ranges(P, 2))
+        run.step()
+        run.step()
+        _same(_snapshot(run), whole, "offloaded save, HBM restore")
+    finally:
+        run.close()

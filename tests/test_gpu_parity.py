@@ -159,6 +159,13 @@ VARIANTS = {
     # parameter dtype different from the gradient dtype
     "bf16_grad_f16_param": dict(base="tiny", numel=RAGGED, n=2, a=2, grad_dtype="bf16", param_dtype="f16",
                                 steps=3),
+    # 3000 tensors of 0 to 700 elements: most shorter than one piece, every
+    # tensor end a ragged tail, a chunk table of thousands of entries
+    "many_tiny_tensors": dict(base="gpt2_small", numel=tuple(int(x) for x in np.random.default_rng(11).integers(
+        0, 701, 3000)), n=3, a=2, max_norm=0.05, scaled_tensors=(7, 2999), steps=3),
+    # the largest chunk size: every tensor here is one chunk of up to 2^18 pieces
+    "max_chunk": dict(base="gpt2_small", numel=RAGGED, n=2, a=3, max_norm=0.05, scaled_tensors=(1,),
+                      chunk=1 << 26, steps=3),
 }
 
 
