@@ -295,7 +295,8 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     nbuf = len(calls) if len(calls) * per_buf <= budget else int(budget // per_buf)
     nbuf = max(nbuf, 2 * w.n if not w.partials else w.n)
     # one allocation; a micro-step's n replicas take consecutive rows
-    bufs = list(torch.empty((nbuf, w.P), dtype=torch.int16, device="cuda").unbind(0))
+    ring = torch.empty((nbuf, w.P), dtype=torch.int16, device="cuda")
+    bufs = list(ring.unbind(0))
     addr = {}
     for i, (r, k) in enumerate(calls):
         b = bufs[i % nbuf]
@@ -346,6 +347,28 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         one_step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    skipped_ms = None
+    if w.injections and not graph:
+        # one step whose g_bar holds an inf, as the workload injects one: the
+        # step is skipped (single pass: computed, then discarded and the
+        # parameters emitted again); the buffer is restored afterwards
+        last = 1 if w.partials else w.a
+        _, r0, _, idx, val = w.injections[0]
+        ptr = addr[(r0 % w.n, last)] + 2 * idx
+        flat = ring.view(-1)
+        pos = (ptr - ring.data_ptr()) // 2
+        saved = flat[pos].clone()
+        torch.cuda.synchronize()
+        synth._poke_u16(ptr, synth._lp_bits(val, w.grad_dtype), stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st_obj)
+        one_step(False)
+        e1.record(st_obj)
+        torch.cuda.synchronize()
+        skipped_ms = e0.elapsed_time(e1)
+        assert d.read_state()["found_inf"] == 1
+        flat[pos] = saved
+        torch.cuda.synchronize()
     if graph:  # the same step as one HIP graph: capture, warm up, time the replays
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st_obj):
@@ -368,6 +391,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     d.close()
     del bufs
     torch.cuda.empty_cache()
+    per_kind["skipped_step_ms"] = skipped_ms
     return elapsed, per_kind, state, ckpt, used_layout
 
 
@@ -522,6 +546,7 @@ def main():
     step_bytes = sum(per_param.values()) * w.P
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    skipped_ms = per_kind.pop("skipped_step_ms", None)
     # dominant kernel: the call kind that moves the most algorithmic bytes per step
     dom = max(per_param, key=lambda k: per_param[k])
     dom_bytes = launch_bytes(w, dom, single)
@@ -565,6 +590,7 @@ def main():
                      "avg_launch_ms": dom_ms},
         "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
+        "skipped_step_ms": skipped_ms,
         "cpu_baseline": None,
     }
     if args.state == "host":
