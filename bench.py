@@ -515,7 +515,7 @@ def cpu_baseline(w, sample: int) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU: the n replicas share its HBM and there is no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     from synth import workloads

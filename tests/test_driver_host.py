@@ -40,3 +40,15 @@ def test_even_shards_tile():
         assert len(sh) == k and sh[0][0] == 0 and sh[-1][1] == P
         assert all(a[1] == b[0] for a, b in zip(sh, sh[1:]))
         assert max(e - b for b, e in sh) - min(e - b for b, e in sh) <= 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any other --gpus value exits with status 2
+    and a message, before anything is allocated."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
