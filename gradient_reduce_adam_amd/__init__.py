@@ -101,8 +101,8 @@ class DpError(RuntimeError):
         self.message = message
 
 
-_STATUS_NAMES = {0: "DP_OK", 1: "DP_ERR_INVALID_ARG", 2: "DP_ERR_BAD_LAYOUT", 3: "DP_ERR_UNBOUND", 4: "DP_ERR_RANGE",
-                 5: "DP_ERR_STATE", 6: "DP_ERR_OOM", 7: "DP_ERR_HIP"}
+_STATUS_NAMES = dict(enumerate(("DP_OK", "DP_ERR_INVALID_ARG", "DP_ERR_BAD_LAYOUT", "DP_ERR_UNBOUND", "DP_ERR_RANGE",
+                                 "DP_ERR_STATE", "DP_ERR_OOM", "DP_ERR_HIP", "DP_ERR_IO", "DP_ERR_CORRUPT")))
 
 
 def _hip_runtimes() -> set:

@@ -121,10 +121,12 @@ dp_status upload_table(dp_plan* p, int64_t begin, int64_t end, DeviceTable* out,
     return DP_OK;
 }
 
+// Every compute call passes through here: the plan's device must be current
+// (kernels get pointers into its memory), and the [0, P) table must exist.
 dp_status ensure_full(dp_plan* p) {
-    if (p->full.dev || p->P == 0 || p->full.count > 0) return DP_OK;
     dp_status s = ensure_device(p);
     if (s != DP_OK) return s;
+    if (p->full.dev || p->P == 0 || p->full.count > 0) return DP_OK;
     return upload_table(p, 0, p->P, &p->full, &p->full_host);
 }
 
@@ -134,13 +136,13 @@ dp_status range_table(dp_plan* p, int64_t begin, int64_t end, const DeviceTable*
         *out = &p->full;
         return s;
     }
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
     for (const DeviceTable& t : p->ranges)
         if (t.begin == begin && t.end == end) {
             *out = &t;
             return DP_OK;
         }
-    dp_status s = ensure_device(p);
-    if (s != DP_OK) return s;
     DeviceTable t;
     s = upload_table(p, begin, end, &t);
     if (s != DP_OK) return s;
@@ -276,6 +278,10 @@ dp_status dp_plan_create(const dp_layout* L, dp_plan** out) {
 dp_status dp_plan_destroy(dp_plan* p) {
     if (!p) return DP_OK;
     if (p->device >= 0) {
+        // free on the plan's device, after its work has drained
+        int cur = -1;
+        const bool switched = hipGetDevice(&cur) == hipSuccess && cur != p->device &&
+                              hipSetDevice(p->device) == hipSuccess;
         (void)hipDeviceSynchronize();
         for (auto& row : p->roles)
             for (auto& b : row)
@@ -288,6 +294,7 @@ dp_status dp_plan_destroy(dp_plan* p) {
         if (p->stats.bad) (void)hipFree(p->stats.bad);
         if (p->fold.sumsq) (void)hipFree(p->fold.sumsq);
         if (p->fold.bad) (void)hipFree(p->fold.bad);
+        if (switched) (void)hipSetDevice(cur);
     }
     delete p;
     return DP_OK;
@@ -365,16 +372,25 @@ dp_status dp_plan_bind_tensors(dp_plan* p, dp_role role, int32_t replica, void* 
     s = ensure_device(p);
     if (s != DP_OK) return s;
     Binding& b = p->roles[role][replica];
-    if (!b.dev_table && p->T > 0) {
+    if (b.dev_table) {
+        // the table is rewritten in place: kernels launched with the old
+        // binding, on any stream, must be done with it
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before rebinding a pointer table");
+    } else if (p->T > 0) {
         hipError_t e = hipMalloc(reinterpret_cast<void**>(&b.dev_table), sizeof(void*) * p->T);
         if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of a pointer table: %s", hipGetErrorString(e));
     }
     b.tensors.assign(ptrs, ptrs + p->T);
+    b.flat = nullptr;
     if (p->T > 0) {
         hipError_t e = hipMemcpy(b.dev_table, b.tensors.data(), sizeof(void*) * p->T, hipMemcpyHostToDevice);
-        if (e != hipSuccess) return hip_fail(e, "hipMemcpy of a pointer table");
+        if (e != hipSuccess) {
+            b.bound = false;  // the device table is not what the host holds
+            b.tensors.clear();
+            return hip_fail(e, "hipMemcpy of a pointer table");
+        }
     }
-    b.flat = nullptr;
     b.bound = true;
     return DP_OK;
 }
@@ -386,6 +402,34 @@ dp_status dp_plan_prepare_range(dp_plan* p, int64_t begin, int64_t end) {
                     static_cast<long long>(end), static_cast<long long>(p->P));
     const DeviceTable* t = nullptr;
     return range_table(p, begin, end, &t);
+}
+
+// The state block and the statistics scratch, all or nothing: on a failure
+// nothing stays allocated and p->state stays null.
+static dp_status alloc_device_state(dp_plan* p) {
+    // statistics are always written on table pieces of [0, P): one slot per
+    // piece, grouped by XCD; the slots no piece maps to stay zero
+    const size_t np = static_cast<size_t>(dpk::stats_slots(std::max<int64_t>(p->full.npieces(false), 1)));
+    const size_t ng = (np + dpk::kFoldGroup - 1) / dpk::kFoldGroup;
+    void* mem[5] = {};
+    const size_t bytes[5] = {sizeof(dpk::DevState), np * sizeof(double), np * sizeof(uint32_t), ng * sizeof(double),
+                             ng * sizeof(uint64_t)};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipMalloc(&mem[i], bytes[i]);
+    if (e == hipSuccess) e = hipMemset(mem[1], 0, bytes[1]);
+    if (e == hipSuccess) e = hipMemset(mem[2], 0, bytes[2]);
+    if (e != hipSuccess) {
+        for (void* m : mem)
+            if (m) (void)hipFree(m);
+        return fail(e == hipErrorOutOfMemory ? DP_ERR_OOM : DP_ERR_HIP,
+                    "allocation of the state block and statistics scratch: %s", hipGetErrorString(e));
+    }
+    p->state = static_cast<dpk::DevState*>(mem[0]);
+    p->stats.sumsq = static_cast<double*>(mem[1]);
+    p->stats.bad = static_cast<uint32_t*>(mem[2]);
+    p->fold.sumsq = static_cast<double*>(mem[3]);
+    p->fold.bad = static_cast<uint64_t*>(mem[4]);
+    return DP_OK;
 }
 
 dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream) {
@@ -404,23 +448,8 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     s = ensure_full(p);
     if (s != DP_OK) return s;
     if (!p->state) {
-        hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->state), sizeof(dpk::DevState));
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of the state block: %s", hipGetErrorString(e));
-        // statistics are always written on table pieces of [0, P): one slot
-        // per piece, grouped by XCD; the slots no piece maps to stay zero
-        const size_t np = static_cast<size_t>(dpk::stats_slots(std::max<int64_t>(p->full.npieces(false), 1)));
-        e = hipMalloc(reinterpret_cast<void**>(&p->stats.sumsq), np * sizeof(double));
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
-        e = hipMalloc(reinterpret_cast<void**>(&p->stats.bad), np * sizeof(uint32_t));
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics partials: %s", hipGetErrorString(e));
-        e = hipMemset(p->stats.sumsq, 0, np * sizeof(double));
-        if (e == hipSuccess) e = hipMemset(p->stats.bad, 0, np * sizeof(uint32_t));
-        if (e != hipSuccess) return hip_fail(e, "hipMemset of statistics partials");
-        const size_t ng = (np + dpk::kFoldGroup - 1) / dpk::kFoldGroup;
-        e = hipMalloc(reinterpret_cast<void**>(&p->fold.sumsq), ng * sizeof(double));
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics groups: %s", hipGetErrorString(e));
-        e = hipMalloc(reinterpret_cast<void**>(&p->fold.bad), ng * sizeof(uint64_t));
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of statistics groups: %s", hipGetErrorString(e));
+        s = alloc_device_state(p);
+        if (s != DP_OK) return s;
     }
     const double scale = cfg->scaler_mode == DP_SCALER_NONE ? 1.0 : cfg->init_scale;
     s = check_launch(dpk::launch_state_init(p->state, scale, stream), "state init launch");
@@ -764,6 +793,8 @@ dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t
 dp_status dp_read_state(dp_plan* p, dp_step_state* out, hipStream_t stream) {
     if (!p || !out) return fail(DP_ERR_INVALID_ARG, "dp_read_state: null argument");
     if (!p->state) return fail(DP_ERR_STATE, "dp_read_state before dp_state_init");
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
     hipError_t e = hipMemcpyAsync(out, p->state, sizeof(dp_step_state), hipMemcpyDeviceToHost, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of the state block");
     e = hipStreamSynchronize(stream);

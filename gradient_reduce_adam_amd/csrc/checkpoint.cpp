@@ -731,8 +731,10 @@ dp_status dp_checkpoint_save(dp_plan* p, const char* dir, int64_t generation, in
                              hipStream_t stream) {
     if (!p || !dir) return fail(DP_ERR_INVALID_ARG, "dp_checkpoint_save: null argument");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_checkpoint_save before dp_state_init");
+    dp_status s = dpapi::ensure_device(p);
+    if (s != DP_OK) return s;
     dpk::DevState st;
-    dp_status s = read_device_state(p, stream, &st);
+    s = read_device_state(p, stream, &st);
     if (s != DP_OK) return s;
     const int bank = st.bank;
     s = device_checks(p, dir, "dp_checkpoint_save", bank);
@@ -752,8 +754,10 @@ dp_status dp_checkpoint_save(dp_plan* p, const char* dir, int64_t generation, in
 dp_status dp_checkpoint_commit(dp_plan* p, const char* dir, int64_t generation, hipStream_t stream) {
     if (!p || !dir) return fail(DP_ERR_INVALID_ARG, "dp_checkpoint_commit: null argument");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_checkpoint_commit before dp_state_init");
+    dp_status s = dpapi::ensure_device(p);
+    if (s != DP_OK) return s;
     dpk::DevState st;
-    dp_status s = read_device_state(p, stream, &st);
+    s = read_device_state(p, stream, &st);
     if (s != DP_OK) return s;
     dp_step_state scalars;
     std::memcpy(&scalars, &st, sizeof(scalars));
@@ -765,22 +769,15 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
                              hipStream_t stream) {
     dp_status s = device_checks(p, dir, "dp_checkpoint_load", 0);
     if (s != DP_OK) return s;
-    dpk::DevState st;
-    s = read_device_state(p, stream, &st);
-    if (s != DP_OK) return s;
-    Pinned stage;
-    s = alloc_pinned(&stage);
-    if (s != DP_OK) return s;
     const dp_layout L = plan_layout(p);
-    bool want[kArrays] = {true, true, true, true};
     dp_step_state saved;
     dp_state_cfg cfg;
-    s = read_range(dir, &L, begin, end, stage.p,
-                   [&](int a, int64_t lo, int64_t hi, const void* src) {
-                       return copy_role(p, *state_binding(p, a, 0), esize(a, p->pdt), lo, hi, const_cast<void*>(src),
-                                        false, stream);
-                   },
-                   want, &saved, &cfg, nullptr);
+    bool want[kArrays] = {false, false, false, false};
+    const PutFn none = [](int, int64_t, int64_t, const void*) { return DP_OK; };
+    // the manifest alone first (an empty range reads no shard): a layout or
+    // settings mismatch fails before any of the plan's memory is written
+    int64_t gen0 = 0, gen1 = 0;
+    s = read_range(dir, &L, begin, begin, nullptr, none, want, &saved, &cfg, &gen0);
     if (s != DP_OK) return s;
     if (restore_scalars) {
         const dp_state_cfg& c = p->cfg;
@@ -788,8 +785,25 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
             (c.scaler_mode == DP_SCALER_DYNAMIC &&
              (cfg.growth_interval != c.growth_interval || cfg.backoff != c.backoff || cfg.growth != c.growth)))
             return fail(DP_ERR_STATE, "the checkpoint was taken with other optimizer settings (betas or loss scaler)");
-        std::memcpy(&st, &saved, sizeof(st));
     }
+    dpk::DevState st;
+    s = read_device_state(p, stream, &st);
+    if (s != DP_OK) return s;
+    Pinned stage;
+    s = alloc_pinned(&stage);
+    if (s != DP_OK) return s;
+    std::fill(want, want + kArrays, true);
+    s = read_range(dir, &L, begin, end, stage.p,
+                   [&](int a, int64_t lo, int64_t hi, const void* src) {
+                       return copy_role(p, *state_binding(p, a, 0), esize(a, p->pdt), lo, hi, const_cast<void*>(src),
+                                        false, stream);
+                   },
+                   want, &saved, &cfg, &gen1);
+    if (s != DP_OK) return s;
+    if (gen1 != gen0)
+        return fail(DP_ERR_STATE, "generation %lld was committed in %s during the load (it began at generation %lld)",
+                    static_cast<long long>(gen1), dir, static_cast<long long>(gen0));
+    if (restore_scalars) std::memcpy(&st, &saved, sizeof(st));
     st.bank = 0;
     hipError_t e = hipMemcpy(p->state, &st, sizeof(st), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "writing the device state");

@@ -106,7 +106,10 @@ dp_status dp_checkpoint_commit(dp_plan* plan, const char* dir, int64_t generatio
  * equal the checkpoint's, else DP_ERR_STATE.  Accumulation restarts: the next
  * call must be a first micro-step.  The call synchronises stream, and
  * allocates and frees pinned host buffers.  Errors are those of dp_ckpt_read,
- * plus DP_ERR_STATE before dp_state_init. */
+ * plus DP_ERR_STATE before dp_state_init.  A layout, range or settings
+ * mismatch is found in the manifest before any of the plan's memory is
+ * written; a corrupt shard block or a generation committed by another writer
+ * during the load (DP_ERR_STATE) can leave the range partly restored. */
 dp_status dp_checkpoint_load(dp_plan* plan, const char* dir, int64_t begin, int64_t end, int32_t restore_scalars,
                              hipStream_t stream);
 

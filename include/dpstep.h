@@ -35,6 +35,10 @@
  *    kernels surface at the next synchronising call (dp_read_state).
  *  - One plan is used from one stream at a time; distinct plans are
  *    independent.
+ *  - A plan belongs to the device that is current at its first GPU call
+ *    (binding per-tensor pointers, preparing a range, dp_state_init).  Every
+ *    later GPU call checks that this device is current, and fails with
+ *    DP_ERR_STATE otherwise.
  */
 #ifndef DPSTEP_H
 #define DPSTEP_H
@@ -173,7 +177,7 @@ const char* dp_last_error(void);
 dp_status dp_plan_create(const dp_layout* layout, dp_plan** out);
 
 /* Frees the library's device memory (tables, partials, state) and the plan.
- * Synchronises the device first.  Null is accepted. */
+ * Synchronises the plan's device first.  Null is accepted. */
 dp_status dp_plan_destroy(dp_plan* plan);
 
 dp_status dp_plan_info_get(const dp_plan* plan, dp_plan_info* out);
@@ -190,8 +194,10 @@ dp_status dp_plan_chunks(const dp_plan* plan, int64_t begin, int64_t end, int64_
 dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* device_base);
 
 /* Binds one device pointer per tensor (host array ptrs[num_tensors]).  The
- * pointer table is copied to the device: this call allocates and
- * synchronises. */
+ * pointer table is copied to the device: the first binding of a role
+ * allocates its table; a rebinding rewrites it in place after synchronising
+ * the device, so work already launched with the old pointers, on any stream,
+ * is finished first.  If the copy fails the role is left unbound. */
 dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
 
 /* Builds and uploads the chunk table of [begin, end) so later dp_adam_step

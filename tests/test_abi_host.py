@@ -33,6 +33,11 @@ def test_abi_version_and_status_strings():
     assert dp.dp_abi_version() == 2
     assert dp.dp_status_string(dp.DP_ERR_RANGE) == "range out of bounds"
     assert dp.dp_status_string(0) == "ok"
+    # every status has a string in the library and a name in the binding
+    for st in range(dp.DP_ERR_CORRUPT + 1):
+        assert dp.dp_status_string(st) != "unknown status"
+        assert dp.DpError(st, "x").args[0].startswith("DP_")
+    assert dp.dp_status_string(dp.DP_ERR_CORRUPT + 1) == "unknown status"
 
 
 @pytest.mark.parametrize("kw", [dict(n_replicas=0), dict(n_replicas=17), dict(grad_dtype="f32"),

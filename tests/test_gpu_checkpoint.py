@@ -167,9 +167,12 @@ def test_load_errors(tmp_path):
         run.close()
     run = GpuRun(w.with_(beta2=0.99))
     try:
+        before = _snapshot(run)
         with pytest.raises(dp.DpError) as e:
             run.d.plan.checkpoint_load(str(tmp_path), restore_scalars=True, stream=run.stream)
         assert e.value.status == dp.DP_ERR_STATE and "optimizer settings" in e.value.message
+        # the mismatch is found before anything is written
+        _same(_snapshot(run), before, "after a refused restore")
     finally:
         run.close()
 
