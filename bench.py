@@ -477,6 +477,40 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
     return lines
 
 
+# hipDeviceAttribute_t values of the ROCm 7 headers
+HIP_ATTR_MEMORY_BUS_WIDTH = 59   # hipDeviceAttributeMemoryBusWidth, bits
+HIP_ATTR_MEMORY_CLOCK_RATE = 60  # hipDeviceAttributeMemoryClockRate, kHz
+
+
+def device_info() -> dict:
+    """What the runtime reports about the device: name, compute units, HBM
+    size, and the memory clock and bus width.  On MI355X the runtime reports
+    a 2 GHz clock for its HBM3E, which moves data at 8 Gb/s per pin: four
+    transfers per reported clock, so clock x 4 x width is the interface's
+    nominal rate (8.19 TB/s), a cross-check of the published 8 TB/s that
+    stays the roofline's denominator."""
+    import ctypes
+
+    import torch
+
+    dev = torch.cuda.current_device()
+    pr = torch.cuda.get_device_properties(dev)
+    info = {"name": pr.name, "arch": pr.gcnArchName, "compute_units": pr.multi_processor_count,
+            "hbm_bytes": pr.total_memory, "mem_clock_khz": None, "mem_bus_bits": None, "nominal_gbps": None}
+    with open("/proc/self/maps") as f:
+        path = next((ln.split()[-1] for ln in f if "libamdhip64" in ln), None)
+    if path:
+        hip = ctypes.CDLL(path)
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_MEMORY_BUS_WIDTH, dev) == 0:
+            info["mem_bus_bits"] = v.value
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_MEMORY_CLOCK_RATE, dev) == 0:
+            info["mem_clock_khz"] = v.value
+        if info["mem_bus_bits"] and info["mem_clock_khz"]:
+            info["nominal_gbps"] = info["mem_clock_khz"] * 1e3 * 4 * info["mem_bus_bits"] / 8 / 1e9
+    return info
+
+
 def cpu_baseline(w, sample: int) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload: one
     full step (all micro-steps, reduction, statistics, update) over `sample`
@@ -591,6 +625,7 @@ def main():
         "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
         "skipped_step_ms": skipped_ms,
+        "device": device_info(),
         "cpu_baseline": None,
     }
     if args.state == "host":
