@@ -27,6 +27,11 @@ dp_status fail(dp_status s, const char* fmt, ...) {
     vsnprintf(buf, sizeof(buf), fmt, ap);
     va_end(ap);
     g_last_error = buf;
+    // The error now belongs to this call's status and message.  Reset the
+    // runtime's per-thread last error, or the caller's next HIP error check
+    // (torch makes one after its own allocations and launches) would report
+    // it again as its own.
+    if (s == DP_ERR_OOM || s == DP_ERR_HIP) (void)hipGetLastError();
     return s;
 }
 

@@ -40,7 +40,8 @@ struct DeviceTable {
     dpk::Table table(bool flat) const { return dpk::Table{dev, begin, end, npieces(flat), log2s, flat}; }
 };
 
-// Records the message of a failure for dp_last_error() and returns s.
+// Records the message of a failure for dp_last_error() and returns s; for
+// DP_ERR_OOM and DP_ERR_HIP it also resets the runtime's last error.
 dp_status fail(dp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 dp_status hip_fail(hipError_t e, const char* what);
 extern thread_local std::string g_last_error;

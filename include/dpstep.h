@@ -31,7 +31,9 @@
  *  - Compute calls are asynchronous on the caller's stream, never synchronise
  *    and never allocate, except where a comment says otherwise.
  *  - Every call returns a dp_status.  On failure nothing was launched and
- *    dp_last_error() returns a message for the calling thread.  Faults inside
+ *    dp_last_error() returns a message for the calling thread.  A failed HIP
+ *    call inside the library is reported there, and hipGetLastError() is
+ *    reset, so the caller's own HIP error checks do not see it again.  Faults inside
  *    kernels surface at the next synchronising call (dp_read_state).
  *  - One plan is used from one stream at a time; distinct plans are
  *    independent.
