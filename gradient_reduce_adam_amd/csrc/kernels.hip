@@ -353,6 +353,15 @@ __global__ void __launch_bounds__(kWave) k_stats(Table t, int64_t base, RoleRef 
 // pass 2: the statistics slots are folded in slot order -- by groups of
 // kFoldGroup when there are many -- and one workgroup updates the scalar state
 // ============================================================================
+// The fixed order: thread t adds slots lo + t, lo + t + 256, ... in turn;
+// then s[t] += s[t + w] for w = 128, 64, ..., 1.  The slots were written from
+// every XCD and miss this one's L2, so a thread issues a batch of loads before
+// it adds them (same order), and the levels below the wave size run as wave-0
+// butterflies: lane t < w then adds s[t] + s[t + w] exactly as the tree does,
+// and lane 0 ends with the tree's sum, bit for bit.  Result in thread 0.
+constexpr int kFoldBatch = 16;  // loads in flight per thread (kFoldGroup / kFoldThreads)
+static_assert(kFoldThreads == 4 * kWave, "the fold has four waves");
+
 template <typename Count>
 __device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, const Count* __restrict__ bad_in,
                                            int64_t lo, int64_t hi, double& ss_out, uint64_t& bad_out) {
@@ -361,22 +370,48 @@ __device__ __forceinline__ void block_fold(const double* __restrict__ ss_in, con
     const int tid = threadIdx.x;
     double ss = 0.0;
     uint64_t bad = 0;
-    for (int64_t i = lo + tid; i < hi; i += kFoldThreads) {
-        ss += ss_in[i];
-        bad += bad_in[i];
+    for (int64_t base = lo + tid; base < hi; base += int64_t{kFoldBatch} * kFoldThreads) {
+        double v[kFoldBatch];
+        uint64_t c[kFoldBatch];
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j) {
+            const int64_t i = base + int64_t{j} * kFoldThreads;
+            v[j] = i < hi ? ss_in[i] : 0.0;
+            c[j] = i < hi ? static_cast<uint64_t>(bad_in[i]) : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j) {
+            if (base + int64_t{j} * kFoldThreads < hi) {
+                ss += v[j];
+                bad += c[j];
+            }
+        }
     }
     s_ss[tid] = ss;
     s_bad[tid] = bad;
     __syncthreads();
-    for (int w = kFoldThreads / 2; w > 0; w >>= 1) {
+#pragma unroll
+    for (int w = kFoldThreads / 2; w >= kWave; w >>= 1) {
         if (tid < w) {
             s_ss[tid] = s_ss[tid] + s_ss[tid + w];
             s_bad[tid] = s_bad[tid] + s_bad[tid + w];
         }
         __syncthreads();
     }
-    ss_out = s_ss[0];
-    bad_out = s_bad[0];
+    if (tid < kWave) {
+        ss = s_ss[tid];
+        bad = s_bad[tid];
+#pragma unroll
+        for (int w = kWave / 2; w > 0; w >>= 1) {
+            // lane t < w: s[t] + s[t + w]; the other lanes only mirror it
+            const double o = __shfl_xor(ss, w, kWave);
+            const uint64_t ob = __shfl_xor(bad, w, kWave);
+            ss = (tid & w) ? o + ss : ss + o;
+            bad += ob;
+        }
+    }
+    ss_out = ss;
+    bad_out = bad;
 }
 
 __global__ void __launch_bounds__(kFoldThreads) k_fold(StatsBuf sb, int64_t nslots, FoldBuf fold) {
