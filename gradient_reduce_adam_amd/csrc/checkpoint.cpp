@@ -12,6 +12,8 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <memory>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -608,12 +610,25 @@ struct Pinned {
     }
 };
 
-dp_status alloc_pinned(Pinned* b) {
-    hipError_t e = hipHostMalloc(&b->p, static_cast<size_t>(kStageElems) * 4, hipHostMallocDefault);
+// Staging sizes, in bytes (binary32 elements; the widest array).  A save of
+// [begin, end) stages at most kStageElems elements at a time; a read of
+// [begin, end) stages the whole checksum blocks around each shard's part of
+// it, which reach at most one block past either end.
+size_t save_staging_bytes(int64_t begin, int64_t end) {
+    const int64_t n = begin >= 0 && end > begin ? end - begin : 1;  // a bad range fails later
+    return static_cast<size_t>(std::min(kStageElems, n)) * 4;
+}
+
+size_t read_staging_bytes(int64_t begin, int64_t end) {
+    const int64_t n = begin >= 0 && end > begin ? end - begin : 0;  // a bad range fails later
+    return static_cast<size_t>(std::min(kStageElems, n + 2 * kBlockElems)) * 4;
+}
+
+dp_status alloc_pinned(Pinned* b, size_t bytes) {
+    hipError_t e = hipHostMalloc(&b->p, bytes, hipHostMallocDefault);
     if (e != hipSuccess) {
         b->p = nullptr;
-        return fail(DP_ERR_OOM, "hipHostMalloc of a %lld-byte staging buffer: %s",
-                    static_cast<long long>(kStageElems * 4), hipGetErrorString(e));
+        return fail(DP_ERR_OOM, "hipHostMalloc of a %zu-byte staging buffer: %s", bytes, hipGetErrorString(e));
     }
     return DP_OK;
 }
@@ -716,8 +731,9 @@ dp_status dp_ckpt_read(const char* dir, const dp_layout* layout, int64_t begin, 
     void* dst[kArrays] = {master, exp_avg, exp_avg_sq, param};
     bool want[kArrays];
     for (int a = 0; a < kArrays; ++a) want[a] = dst[a] != nullptr;
-    std::vector<char> staging(static_cast<size_t>(kStageElems) * 4);
-    return read_range(dir, layout, begin, end, staging.data(),
+    std::unique_ptr<char[]> staging(new (std::nothrow) char[read_staging_bytes(begin, end)]);
+    if (!staging) return fail(DP_ERR_OOM, "dp_ckpt_read: host allocation of the staging buffer failed");
+    return read_range(dir, layout, begin, end, staging.get(),
                       [&](int a, int64_t lo, int64_t hi, const void* src) {
                           const size_t es = esize(a, layout->param_dtype);
                           std::memcpy(static_cast<char*>(dst[a]) + (lo - begin) * es, src,
@@ -740,7 +756,7 @@ dp_status dp_checkpoint_save(dp_plan* p, const char* dir, int64_t generation, in
     s = device_checks(p, dir, "dp_checkpoint_save", bank);
     if (s != DP_OK) return s;
     Pinned stage;
-    s = alloc_pinned(&stage);
+    s = alloc_pinned(&stage, save_staging_bytes(begin, end));
     if (s != DP_OK) return s;
     const dp_layout L = plan_layout(p);
     return write_shard(dir, generation, &L, begin, end, stage.p,
@@ -790,7 +806,7 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
     s = read_device_state(p, stream, &st);
     if (s != DP_OK) return s;
     Pinned stage;
-    s = alloc_pinned(&stage);
+    s = alloc_pinned(&stage, read_staging_bytes(begin, end));
     if (s != DP_OK) return s;
     std::fill(want, want + kArrays, true);
     s = read_range(dir, &L, begin, end, stage.p,
