@@ -3,8 +3,8 @@
  * MI355X (gfx950).
  *
  * The step, as the pages define it:
- *  - every replica r holds the full model and accumulates the gradients of
- *    its a micro-steps into g_r, with no communication in between
+ *  - every replica r holds the full model and sums its own gradients over
+ *    a micro-steps into g_r, exchanging nothing until the last one
  *    ("Distributed Training: Split along the Four Axes of Data, Tensor,
  *    Pipeline, and State", ai-knowledge-map.com: averaging-formula paragraph
  *    and the b=4, a=8, n=8 worked example);

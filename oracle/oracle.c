@@ -119,9 +119,9 @@ void oracle_narrow(const float* src, int dtype, int64_t n, uint16_t* out) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* step 1: micro-step accumulation  [DT, averaging formula: "each rank       */
-/* accumulates the gradients of its a micro-steps to obtain g_r"; worked     */
-/* example: no communication during accumulation]                            */
+/* step 1: micro-step accumulation  [DT, averaging formula: replica r sums  */
+/* its own gradients over the a micro-steps into g_r; worked example: the    */
+/* replicas exchange nothing until the last micro-step]                      */
 /* ------------------------------------------------------------------------ */
 /* acc <- g (first micro-step) or acc + g, stored in binary32. */
 void oracle_accumulate(float* acc, const void* g, int gdtype, int64_t n, int first) {
