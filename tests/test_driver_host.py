@@ -52,3 +52,32 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name,two_pass,single,unfused", [
+    ("tiny", 82, 74, 114), ("gpt2_small", 610, 602, 674), ("zero3_rank_7b", 50, 42, 50),
+    ("unsharded_7b", 106, 98, 106), ("tp_column_slice", 162, 154, 194)])
+def test_bench_byte_model(name, two_pass, single, unfused):
+    """The bytes per parameter and step that bench.py divides by the step
+    time, against closed forms.  Unfused: the first micro-step writes the
+    binary32 accumulator, every later one reads and writes it, the reduction
+    reads it, g_bar is written and read back, and the update moves 30 B:
+    n a (s_g + 8) + 34 with n >= 2 accumulators, a (s_g + 8) + 26 for one
+    replica (g_bar is the accumulator), n s_g + 34 for incoming partials.
+    This library fuses the last micro-step into the tree, so that
+    accumulator is neither written back nor read again (8 B less per
+    replica), and the single pass never stores g_bar (8 B less)."""
+    import bench
+    w = workloads.by_name(name)
+    sg = 2
+    if w.partials:
+        ref_unfused = w.n * sg + 34
+    elif w.n == 1:
+        ref_unfused = w.a * (sg + 8) + 26
+    else:
+        ref_unfused = w.n * w.a * (sg + 8) + 34
+    assert bench.unfused_bytes_per_param(w) == ref_unfused == unfused
+    assert sum(bench.bytes_model(w, False).values()) == two_pass
+    assert sum(bench.bytes_model(w, True).values()) == single == two_pass - 8
+    if not w.partials and w.n > 1:
+        assert unfused - two_pass == w.n * 8
