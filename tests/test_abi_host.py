@@ -83,6 +83,29 @@ def test_chunk_table_matches_brute_force(numel, chunk):
             assert [tuple(int(x) for x in r) for r in got] == ref
 
 
+try:
+    from hypothesis import given, settings, strategies as st
+except ImportError:  # pragma: no cover
+    given = None
+
+if given is not None:
+    @settings(max_examples=300, deadline=None)
+    @given(numel=st.lists(st.integers(0, 5000), max_size=12), log2c=st.integers(8, 13),
+           cut=st.tuples(st.floats(0, 1), st.floats(0, 1)))
+    def test_chunk_table_property(numel, log2c, cut):
+        """Random ragged layouts (empty tensors included), every power-of-two
+        chunk size from 256 to 8192, random ranges: the library's table equals
+        the brute-force one, and its chunks tile the range."""
+        chunk = 1 << log2c
+        P = sum(numel)
+        b, e = sorted(int(c * P) for c in cut)
+        with dp.Plan(numel, 1, "bf16", "bf16", chunk) as p:
+            got = [tuple(int(x) for x in r) for r in p.chunks(b, e)]
+        assert got == _brute_chunks(numel, chunk, b, e)
+        assert sum(r[3] for r in got) == e - b
+        assert all(0 < r[3] <= chunk for r in got)
+
+
 def test_chunk_table_of_a_2pow32_tensor_uses_64bit_indices():
     with dp.Plan((1 << 32, 7), 4, "f16", "f16", 65536) as p:
         c = p.chunks()
