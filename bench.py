@@ -70,6 +70,10 @@ def parse():
                          "reduction in buckets of these sizes, sequential and overlapped on a second stream; "
                          "one JSON line per bucket size")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per micro-batch of the synthetic backward")
+    ap.add_argument("--log-steps", default="", metavar="FILE",
+                    help="after everything timed, run --steps more steps, each followed by a read of the scalar "
+                         "state (a synchronisation), and write one JSON line per step to FILE: t, iter, found_inf, "
+                         "the loss scale, the norm, the clip factor and the time of each call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -246,7 +250,7 @@ def measure_pcie_copies(nbytes: int = 1 << 30, reps: int = 5) -> dict:
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
             ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct",
-            layout: str = "auto"):
+            layout: str = "auto", log_path: str = ""):
     import torch
 
     import synth
@@ -307,6 +311,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
 
     plan = d.plan
     events = {}
+    sink = [events]  # where timed() records: the timed run's events, or one logged step's
 
     def timed(kind, fn, rec):
         if rec:
@@ -315,7 +320,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
             e0.record(st_obj)
             fn()
             e1.record(st_obj)
-            events.setdefault(kind, []).append((e0, e1))
+            sink[0].setdefault(kind, []).append((e0, e1))
         else:
             fn()
 
@@ -382,6 +387,18 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     state = d.read_state()
+    if log_path:  # per-step records, outside everything timed above
+        with open(log_path, "w") as f:
+            for _ in range(steps):
+                sink[0] = {}
+                one_step(True)
+                s_ = d.read_state()  # synchronises the stream
+                ms = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in sink[0].items()}
+                f.write(json.dumps({"workload": w.name, "t": s_["t"], "iter": s_["iter"], "found_inf": s_["found_inf"],
+                                    "scale": s_["scale"], "norm": s_["norm"], "clip": s_["clip"], "call_ms": ms,
+                                    "step_ms": sum(ms.values()),
+                                    "params_per_s": w.P / (sum(ms.values()) * 1e-3)}) + "\n")
+        sink[0] = events
     ckpt = measure_checkpoint(d, ckpt_dir) if ckpt_dir else None
     per_kind = {}
     for kind, pairs in events.items():
@@ -574,7 +591,7 @@ def main():
     single = single_pass_for(w, args.update)
     elapsed, per_kind, state, ckpt, layout = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
                                                      args.bind, single, args.checkpoint_dir, args.state, args.graph,
-                                                     args.offload, args.layout)
+                                                     args.offload, args.layout, args.log_steps)
     ms_per_step = elapsed * 1e3 / args.steps
     per_param = bytes_model(w, single)
     step_bytes = sum(per_param.values()) * w.P
