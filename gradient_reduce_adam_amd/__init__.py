@@ -39,7 +39,7 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 # every exported symbol of dpstep.h
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
-           "dp_plan_prepare_range", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
+           "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
            "dp_accumulate_reduce_range",
            "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
@@ -143,6 +143,7 @@ def _load():
         "dp_plan_bind_flat": (ctypes.c_int, [vp, ctypes.c_int, i32, vp]),
         "dp_plan_bind_tensors": (ctypes.c_int, [vp, ctypes.c_int, i32, PP]),
         "dp_plan_prepare_range": (ctypes.c_int, [vp, i64, i64]),
+        "dp_plan_drop_ranges": (ctypes.c_int, [vp]),
         "dp_state_init": (ctypes.c_int, [vp, ctypes.POINTER(StateCfg), vp]),
         "dp_accumulate": (ctypes.c_int, [vp, i32, i32, i32, vp]),
         "dp_accumulate_all": (ctypes.c_int, [vp, i32, vp]),
@@ -251,6 +252,10 @@ def dp_plan_bind_tensors(plan: int, role: int, replica: int, ptrs: Iterable) -> 
 
 def dp_plan_prepare_range(plan: int, begin: int, end: int) -> None:
     _check(lib.dp_plan_prepare_range(ctypes.c_void_p(plan), begin, end))
+
+
+def dp_plan_drop_ranges(plan: int) -> None:
+    _check(lib.dp_plan_drop_ranges(ctypes.c_void_p(plan)))
 
 
 def dp_state_init(plan: int, beta1: float, beta2: float, scaler: str = "none", init_scale: float = 1.0,
@@ -429,6 +434,9 @@ class Plan:
 
     def prepare_range(self, begin: int, end: int) -> None:
         dp_plan_prepare_range(self.handle, begin, end)
+
+    def drop_ranges(self) -> None:
+        dp_plan_drop_ranges(self.handle)
 
     def state_init(self, beta1: float = 0.9, beta2: float = 0.999, scaler: str = "none", init_scale: float = 1.0,
                    backoff: float = 0.5, growth: float = 2.0, growth_interval: int = 2000, stream=None) -> None:

@@ -437,6 +437,19 @@ static dp_status alloc_device_state(dp_plan* p) {
     return DP_OK;
 }
 
+dp_status dp_plan_drop_ranges(dp_plan* p) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_plan_drop_ranges: null plan");
+    if (p->ranges.empty()) return DP_OK;
+    dp_status s = ensure_device(p);
+    if (s != DP_OK) return s;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before freeing range tables");
+    for (const DeviceTable& t : p->ranges)
+        if (t.dev) (void)hipFree(t.dev);
+    p->ranges.clear();
+    return DP_OK;
+}
+
 dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream) {
     if (!p || !cfg) return fail(DP_ERR_INVALID_ARG, "dp_state_init: null argument");
     if (cfg->scaler_mode < DP_SCALER_NONE || cfg->scaler_mode > DP_SCALER_DYNAMIC)

@@ -203,8 +203,16 @@ dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* 
 dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
 
 /* Builds and uploads the chunk table of [begin, end) so later dp_adam_step
- * calls on that range do not allocate (allocates; synchronises). */
+ * calls on that range do not allocate (allocates; synchronises).  A range's
+ * table stays cached until dp_plan_drop_ranges or dp_plan_destroy. */
 dp_status dp_plan_prepare_range(dp_plan* plan, int64_t begin, int64_t end);
+
+/* Frees the cached chunk tables of every range other than [0, P) (those of
+ * dp_plan_prepare_range and of dp_adam_step calls), for callers whose shard
+ * ranges change over a run.  Synchronises the device first, since launched
+ * kernels may still read them; a later call on such a range builds its table
+ * again.  Nothing else of the plan changes. */
+dp_status dp_plan_drop_ranges(dp_plan* plan);
 
 /* Allocates the device state and statistics scratch on the current device
  * (first call), and sets t = 0, beta powers = 1, scale = init_scale (1 with

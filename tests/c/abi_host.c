@@ -74,6 +74,8 @@ int main(int argc, char** argv) {
     dp_adam_hparams hp = {1e-3, 1e-8, 0.01};
     CHECK(dp_adam_step(plan, &hp, 0, 21003, NULL) == DP_ERR_STATE);
     CHECK(dp_adam_step(plan, &hp, 0, 21004, NULL) == DP_ERR_RANGE);
+    CHECK(dp_plan_drop_ranges(plan) == DP_OK); /* nothing cached: no GPU work */
+    CHECK(dp_plan_drop_ranges(NULL) == DP_ERR_INVALID_ARG);
     CHECK(dp_plan_destroy(plan) == DP_OK);
 
     /* rejected layouts */

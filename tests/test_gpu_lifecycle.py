@@ -1,13 +1,15 @@
 """The plan's life cycle on the GPU, through the C ABI: a failed allocation of
-the state leaves nothing behind and the plan usable for error reporting, and
+the state leaves nothing behind and the plan usable for error reporting;
 per-tensor pointer tables rebound between launches on a non-default stream
-never reach a kernel that was launched with the old ones."""
+never reach a kernel that was launched with the old ones; and cached range
+tables can be dropped when the shard partition changes during a run."""
 import numpy as np
 import pytest
 import torch
 
 import gradient_reduce_adam_amd as dp
 import synth
+from gradient_reduce_adam_amd import driver
 from synth import workloads
 
 from gpu_common import assert_scalars_match, assert_state_close, log, oracle_run
@@ -96,3 +98,35 @@ def test_rebinding_pointer_tables_between_launches():
     ref = oracle_run(w, w.steps)
     assert_scalars_match(state, ref.scalars[-1], where="rebound tables")
     assert_state_close(got, ref.state[(0, P)], where="rebound tables")
+
+
+def test_shard_ranges_change_over_a_run():
+    """The update runs over 3 shard ranges for two steps; the cached range
+    tables are dropped and the next two steps run over 5 other ranges.  The
+    result is the oracle's: a partition of the range never changes the
+    update, and dropped tables are rebuilt on demand."""
+    w = workloads.tiny().with_(numel=(3000, 17, 70001, 4096, 131075), n=2, a=2, steps=4)
+    P = w.P
+    d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
+                      weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2)
+    s = d.stream.cuda_stream
+    d.set_master(lambda ptr: synth.master_device(w, ptr, s))
+    slots = [torch.empty(P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
+
+    def produce(step, r, k, scale):
+        synth.grad_device(w, step, r, k, slots[r].data_ptr(), scale, s)
+        return slots[r].data_ptr()
+
+    try:
+        for shards in (driver.even_shards(P, 3), driver.even_shards(P, 5)):
+            d.plan.drop_ranges()
+            d.shards = shards
+            for _ in range(2):
+                state = d.step(produce)
+        got = {"w": d.master.cpu().numpy(), "m": d.exp_avg.cpu().numpy(), "v": d.exp_avg_sq.cpu().numpy(),
+               "p": d.param.view(torch.int16).cpu().numpy().view(np.uint16)}
+    finally:
+        d.close()
+    ref = oracle_run(w, 4)
+    assert_scalars_match(state, ref.scalars[-1], where="changing shards")
+    assert_state_close(got, ref.state[(0, P)], where="changing shards")
