@@ -412,8 +412,10 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     return elapsed, per_kind, state, ckpt, used_layout
 
 
-def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
-    """The bucketed reduction overlapped with a synthetic backward pass."""
+def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: bool = False):
+    """The bucketed reduction overlapped with a synthetic backward pass; with
+    single, each bucket's reduction also updates its parameters (the single
+    pass in buckets)."""
     import torch
 
     import synth
@@ -423,7 +425,7 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
     d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                       weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                       scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
-                      growth_interval=w.growth_interval, partials=w.partials)
+                      growth_interval=w.growth_interval, partials=w.partials, single_pass=single)
     st = d.stream.cuda_stream
     d.set_master(lambda ptr: synth.master_device(w, ptr, st))
     wi = w.with_(injections=())
@@ -452,19 +454,24 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
     for _ in range(3):  # the last micro-step's reduction as the step issues it (after earlier micro-steps)
         if last > 1:
             d.plan.accumulate_all(first=True, stream=st)
-        reds.append(timed(lambda: d.plan.accumulate_reduce(stream=st), 1))
+        if single:  # the reduction, the statistics and the update in one pass
+            reds.append(timed(lambda: d.plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=st), 1))
+        else:
+            reds.append(timed(lambda: d.plan.accumulate_reduce(stream=st), 1))
     t_red = sum(reds) / len(reds)
     d.close()
     rs = torch.cuda.Stream()
     lines = []
     for mb in bucket_mbs:
-        buckets = driver.backward_buckets(w.numel, int(mb * (1 << 20)))
+        # incoming partials arrive from the exchange in pieces: their buckets
+        # may cut tensors; a backward pass finishes whole tensors
+        buckets = driver.backward_buckets(w.numel, int(mb * (1 << 20)), split=w.partials)
         res, last_ms = {}, {}
         for mode in ("sequential", "overlapped"):
             d = driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
                               weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
                               scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
-                              growth_interval=w.growth_interval, partials=w.partials)
+                              growth_interval=w.growth_interval, partials=w.partials, single_pass=single)
             d.set_master(lambda ptr: synth.master_device(w, ptr, d.stream.cuda_stream))
             marks = []
 
@@ -481,9 +488,12 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int):
             last_ms[mode] = sum(a.elapsed_time(b) for a, b in marks) / len(marks)
             d.close()
         saved = last_ms["sequential"] - last_ms["overlapped"]
-        lines.append({"metric": "last micro-step (synthetic backward + replica reduction) with the reduction "
+        what = "replica reduction and update" if single else "replica reduction"
+        lines.append({"metric": f"last micro-step (synthetic backward + {what}) with the {what} "
                                 "in buckets, sequential and overlapped on a second stream", "unit": "ms",
-                      "config": {"workload": w.name, "bucket_mb": mb, "buckets": len(buckets), "tokens": tokens},
+                      "config": {"workload": w.name, "bucket_mb": mb, "buckets": len(buckets), "tokens": tokens,
+                                 "buckets_cut_tensors": bool(w.partials),
+                                 "update": "single-pass" if single else "two-pass"},
                       "last_micro_step_sequential_ms": last_ms["sequential"],
                       "last_micro_step_overlapped_ms": last_ms["overlapped"], "saved_ms": saved,
                       "step_sequential_ms": res["sequential"], "step_overlapped_ms": res["overlapped"],
@@ -583,12 +593,12 @@ def main():
         print(json.dumps(res, indent=1))
         return
     w = workloads.by_name(args.workload)
+    single = single_pass_for(w, args.update)
     if args.overlap:
         for line in run_overlap(w, args.steps, args.warmup, [float(x) for x in args.overlap.split(",")],
-                                args.tokens):
+                                args.tokens, single):
             print(json.dumps(line), flush=True)
         return
-    single = single_pass_for(w, args.update)
     elapsed, per_kind, state, ckpt, layout = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
                                                      args.bind, single, args.checkpoint_dir, args.state, args.graph,
                                                      args.offload, args.layout, args.log_steps)

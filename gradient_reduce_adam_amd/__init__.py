@@ -41,7 +41,8 @@ EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_creat
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
            "dp_accumulate_reduce_range",
-           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_read_state",
+           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_range",
+           "dp_reduce_adam_finish", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
            "dp_checkpoint_load")
 
@@ -153,6 +154,8 @@ def _load():
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
         "dp_reduce_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), vp]),
+        "dp_reduce_adam_range": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
+        "dp_reduce_adam_finish": (ctypes.c_int, [vp, vp]),
         "dp_read_state": (ctypes.c_int, [vp, ctypes.POINTER(StepState), vp]),
         "dp_ckpt_write_shard": (ctypes.c_int, [ctypes.c_char_p, i64, ctypes.POINTER(Layout), i64, i64, vp, vp, vp,
                                                vp]),
@@ -300,6 +303,17 @@ def dp_adam_step(plan: int, lr: float, eps: float, weight_decay: float, shard_be
 def dp_reduce_adam_step(plan: int, lr: float, eps: float, weight_decay: float, stream=None) -> None:
     hp = AdamHparams(lr, eps, weight_decay)
     _check(lib.dp_reduce_adam_step(ctypes.c_void_p(plan), ctypes.byref(hp), ctypes.c_void_p(_stream(stream))))
+
+
+def dp_reduce_adam_range(plan: int, lr: float, eps: float, weight_decay: float, begin: int, end: int,
+                         stream=None) -> None:
+    hp = AdamHparams(lr, eps, weight_decay)
+    _check(lib.dp_reduce_adam_range(ctypes.c_void_p(plan), ctypes.byref(hp), begin, end,
+                                    ctypes.c_void_p(_stream(stream))))
+
+
+def dp_reduce_adam_finish(plan: int, stream=None) -> None:
+    _check(lib.dp_reduce_adam_finish(ctypes.c_void_p(plan), ctypes.c_void_p(_stream(stream))))
 
 
 def dp_read_state(plan: int, stream=None) -> dict:
@@ -466,6 +480,13 @@ class Plan:
 
     def reduce_adam_step(self, lr: float, eps: float, weight_decay: float, stream=None) -> None:
         dp_reduce_adam_step(self.handle, lr, eps, weight_decay, stream)
+
+    def reduce_adam_range(self, lr: float, eps: float, weight_decay: float, begin: int, end: int,
+                          stream=None) -> None:
+        dp_reduce_adam_range(self.handle, lr, eps, weight_decay, begin, end, stream)
+
+    def reduce_adam_finish(self, stream=None) -> None:
+        dp_reduce_adam_finish(self.handle, stream)
 
     def read_state(self, stream=None) -> dict:
         return dp_read_state(self.handle, stream)

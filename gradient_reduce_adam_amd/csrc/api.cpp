@@ -195,7 +195,9 @@ bool all_flat(const dpk::StateRefs& s) {
 // half done.
 dp_status no_open_buckets(const dp_plan* p, const char* where) {
     if (!p->buckets.empty())
-        return fail(DP_ERR_STATE, "%s while a bucketed reduction covers %lld of %lld elements", where,
+        return fail(DP_ERR_STATE, "%s while a bucketed %s covers %lld of %lld elements", where,
+                    p->bucket_mode == 2 ? "single pass (dp_reduce_adam_range, then dp_reduce_adam_finish)"
+                                        : "reduction",
                     static_cast<long long>(p->bucket_elems), static_cast<long long>(p->P));
     return DP_OK;
 }
@@ -214,6 +216,31 @@ int64_t piece_at(const dp_plan* p, int64_t x) {
     const int64_t off = x - c.flat;
     if (off >= c.len || off % dpk::kPiece != 0) return -1;
     return (static_cast<int64_t>(it - 1 - ch.begin()) << p->full.log2s) + off / dpk::kPiece;
+}
+
+// A bucket [begin, end) of a bucketed call: inside [0, P), both ends on the
+// piece grid of the [0, P) table, and disjoint from the buckets already done.
+// Its pieces go to *p0, *p1 (when not null).
+dp_status bucket_span(dp_plan* p, int64_t begin, int64_t end, int64_t* p0, int64_t* p1) {
+    if (begin < 0 || end > p->P || begin > end)
+        return fail(DP_ERR_RANGE, "bucket [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
+                    static_cast<long long>(end), static_cast<long long>(p->P));
+    dp_status s = ensure_full(p);
+    if (s != DP_OK) return s;
+    const int64_t q0 = piece_at(p, begin), q1 = piece_at(p, end);
+    if (q0 < 0 || q1 < 0)
+        return fail(DP_ERR_INVALID_ARG,
+                    "bucket [%lld, %lld): each end must be a tensor start, P, or a multiple of 256 elements into "
+                    "its tensor",
+                    static_cast<long long>(begin), static_cast<long long>(end));
+    for (const auto& b : p->buckets)
+        if (begin < b.second && b.first < end)
+            return fail(DP_ERR_STATE, "bucket [%lld, %lld) overlaps bucket [%lld, %lld) of this reduction",
+                        static_cast<long long>(begin), static_cast<long long>(end),
+                        static_cast<long long>(b.first), static_cast<long long>(b.second));
+    if (p0) *p0 = q0;
+    if (p1) *p1 = q1;
+    return DP_OK;
 }
 
 }  // namespace
@@ -479,6 +506,7 @@ dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream)
     p->stats_current = false;
     p->buckets.clear();
     p->bucket_elems = 0;
+    p->bucket_mode = 0;
     return DP_OK;
 }
 
@@ -614,22 +642,11 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
 dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce_range: null plan");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce_range before dp_state_init");
-    if (begin < 0 || end > p->P || begin > end)
-        return fail(DP_ERR_RANGE, "bucket [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
-                    static_cast<long long>(end), static_cast<long long>(p->P));
-    dp_status s = ensure_full(p);
+    if (p->bucket_mode == 2 && !p->buckets.empty())
+        return fail(DP_ERR_STATE, "dp_accumulate_reduce_range while a bucketed single pass is open");
+    dp_status s = bucket_span(p, begin, end, nullptr, nullptr);
     if (s != DP_OK) return s;
     const int64_t p0 = piece_at(p, begin), p1 = piece_at(p, end);
-    if (p0 < 0 || p1 < 0)
-        return fail(DP_ERR_INVALID_ARG,
-                    "bucket [%lld, %lld): each end must be a tensor start, P, or a multiple of 256 elements into "
-                    "its tensor",
-                    static_cast<long long>(begin), static_cast<long long>(end));
-    for (const auto& b : p->buckets)
-        if (begin < b.second && b.first < end)
-            return fail(DP_ERR_STATE, "bucket [%lld, %lld) overlaps bucket [%lld, %lld) of this reduction",
-                        static_cast<long long>(begin), static_cast<long long>(end),
-                        static_cast<long long>(b.first), static_cast<long long>(b.second));
     const Binding* gb = gbar_binding(p);
     if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
     dpk::Srcs grads{}, accs{};
@@ -655,12 +672,14 @@ dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hip
     if (end > begin) {
         p->buckets.emplace_back(begin, end);
         p->bucket_elems += end - begin;
+        p->bucket_mode = 1;
     }
     p->partials_valid = false;
     p->stats_current = false;
     if (p->bucket_elems == p->P) {  // the buckets cover [0, P): the reduction is complete
         p->buckets.clear();
         p->bucket_elems = 0;
+        p->bucket_mode = 0;
         std::fill(p->micro.begin(), p->micro.end(), 0);
         p->partials_valid = true;
         p->partials_count = t.npieces;
@@ -752,25 +771,19 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
                         "adamw launch");
 }
 
-dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t stream) {
-    if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_step: null argument");
-    {
-        dp_status g = no_open_buckets(p, "dp_reduce_adam_step");
-        if (g != DP_OK) return g;
-    }
-    if (!(hp->lr >= 0.0) || !(hp->eps > 0.0) || !(hp->weight_decay >= 0.0))
-        return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
-    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_step before dp_state_init");
-    dpk::Srcs grads{}, accs{};
-    dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+// The single pass's sources (every replica's last micro-step, plus its
+// accumulator after earlier micro-steps) and the state it reads and writes
+// (both banks and the parameters), checked before any launch.
+static dp_status single_pass_sources(dp_plan* p, dpk::Srcs* grads, dpk::Srcs* accs, bool* with_acc) {
+    dp_status s = bound_replicas(p, DP_ROLE_GRAD, grads);
     if (s != DP_OK) return s;
     for (int32_t r = 0; r < p->n; ++r)
         if (p->micro[r] != p->micro[0])
             return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
                         p->micro[r], p->micro[0]);
-    const bool with_acc = p->micro[0] > 0;
-    if (with_acc) {
-        s = bound_replicas(p, DP_ROLE_ACC, &accs);
+    *with_acc = p->micro[0] > 0;
+    if (*with_acc) {
+        s = bound_replicas(p, DP_ROLE_ACC, accs);
         if (s != DP_OK) return s;
     }
     static const char* const names[] = {"MASTER", "EXP_AVG", "EXP_AVG_SQ"};
@@ -779,24 +792,35 @@ dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t
             if (!p->roles[role][b].bound)
                 return fail(DP_ERR_UNBOUND, "role %s bank %d is not bound (the single pass writes the other bank)",
                             names[role - DP_ROLE_MASTER], b);
-    s = need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
-    if (s != DP_OK) return s;
-    s = ensure_full(p);
-    if (s != DP_OK) return s;
+    return need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
+}
+
+static bool valid_hparams(const dp_adam_hparams* hp) {
+    return hp->lr >= 0.0 && hp->eps > 0.0 && hp->weight_decay >= 0.0;
+}
+
+// The single pass over pieces [p0, p1) of the [0, P) table.
+static dp_status single_pass_launch(dp_plan* p, const dp_adam_hparams* hp, bool with_acc, const dpk::Srcs& grads,
+                                    const dpk::Srcs& accs, int64_t p0, int64_t p1, hipStream_t stream) {
+    if (p1 <= p0) return DP_OK;
+    const dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
+    return check_launch(dpk::launch_reduce_adamw(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
+                                                 p->gdt, p->pdt, p->n, p->full.table(false), dpk::PieceSpan{p0, p1},
+                                                 accs, grads, state_refs(p), p->roles[DP_ROLE_PARAM][0].ref(),
+                                                 p->stats, p->state, a, stream),
+                        "reduce + adamw launch");
+}
+
+// The end of a single pass: the statistics fold and the commit of the step
+// (the written bank becomes current if it is applied), then the parameters
+// emitted again from the current bank if it was skipped.
+static dp_status single_pass_commit(dp_plan* p, hipStream_t stream) {
     const dpk::StateRefs sr = state_refs(p);
     const dpk::RoleRef pr = p->roles[DP_ROLE_PARAM][0].ref();
-    const dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
-    const dpk::Table t = p->full.table(false);  // statistics: table pieces
-    if (t.npieces > 0) {
-        s = check_launch(dpk::launch_reduce_adamw(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
-                                                  p->gdt, p->pdt, p->n, t, accs, grads, sr, pr, p->stats, p->state, a,
-                                                  stream),
-                         "reduce + adamw launch");
-        if (s != DP_OK) return s;
-    }
     const dpk::ScalerArgs sc{p->cfg.beta1, p->cfg.beta2, p->cfg.backoff, p->cfg.growth, 0.0,
                              p->cfg.scaler_mode, p->cfg.growth_interval, 1};
-    s = check_launch(dpk::launch_finalize(p->stats, t.npieces, p->fold, p->state, sc, stream), "finalize launch");
+    dp_status s = check_launch(dpk::launch_finalize(p->stats, p->full.npieces(false), p->fold, p->state, sc, stream),
+                               "finalize launch");
     if (s != DP_OK) return s;
     s = check_launch(dpk::launch_restore_param(p->pdt, p->full.table(all_flat(sr) && all_flat({pr})), sr, pr, p->state,
                                                stream),
@@ -805,6 +829,81 @@ dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t
     std::fill(p->micro.begin(), p->micro.end(), 0);
     p->partials_valid = false;
     p->stats_current = false;
+    return DP_OK;
+}
+
+dp_status dp_reduce_adam_step(dp_plan* p, const dp_adam_hparams* hp, hipStream_t stream) {
+    if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_step: null argument");
+    {
+        dp_status g = no_open_buckets(p, "dp_reduce_adam_step");
+        if (g != DP_OK) return g;
+    }
+    if (!valid_hparams(hp)) return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_step before dp_state_init");
+    dpk::Srcs grads{}, accs{};
+    bool with_acc = false;
+    dp_status s = single_pass_sources(p, &grads, &accs, &with_acc);
+    if (s != DP_OK) return s;
+    s = ensure_full(p);
+    if (s != DP_OK) return s;
+    s = single_pass_launch(p, hp, with_acc, grads, accs, 0, p->full.npieces(false), stream);
+    if (s != DP_OK) return s;
+    return single_pass_commit(p, stream);
+}
+
+dp_status dp_reduce_adam_range(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int64_t end,
+                               hipStream_t stream) {
+    if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_range: null argument");
+    if (!valid_hparams(hp)) return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_range before dp_state_init");
+    if (p->bucket_mode == 1 && !p->buckets.empty())
+        return fail(DP_ERR_STATE, "dp_reduce_adam_range while a bucketed reduction is half done");
+    if (p->bucket_mode == 2 && !p->buckets.empty()) {
+        const dp_adam_hparams& h = p->bucket_hp;
+        if (h.lr != hp->lr || h.eps != hp->eps || h.weight_decay != hp->weight_decay)
+            return fail(DP_ERR_INVALID_ARG, "the buckets of one step take the same lr, eps and weight_decay");
+    }
+    int64_t p0 = 0, p1 = 0;
+    dp_status s = bucket_span(p, begin, end, &p0, &p1);
+    if (s != DP_OK) return s;
+    dpk::Srcs grads{}, accs{};
+    bool with_acc = false;
+    s = single_pass_sources(p, &grads, &accs, &with_acc);
+    if (s != DP_OK) return s;
+    s = single_pass_launch(p, hp, with_acc, grads, accs, p0, p1, stream);
+    if (s != DP_OK) return s;
+    if (end > begin) {
+        if (p->buckets.empty()) p->bucket_hp = *hp;
+        p->buckets.emplace_back(begin, end);
+        p->bucket_elems += end - begin;
+        p->bucket_mode = 2;
+    }
+    p->partials_valid = false;
+    p->stats_current = false;
+    return DP_OK;
+}
+
+dp_status dp_reduce_adam_finish(dp_plan* p, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_finish: null plan");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_finish before dp_state_init");
+    if (p->bucket_mode == 1 && !p->buckets.empty())
+        return fail(DP_ERR_STATE, "dp_reduce_adam_finish while a bucketed reduction is half done");
+    if (p->bucket_elems != p->P)
+        return fail(DP_ERR_STATE, "dp_reduce_adam_finish: the buckets cover %lld of %lld elements",
+                    static_cast<long long>(p->bucket_elems), static_cast<long long>(p->P));
+    static const char* const names[] = {"MASTER", "EXP_AVG", "EXP_AVG_SQ"};
+    for (int role = DP_ROLE_MASTER; role <= DP_ROLE_EXP_AVG_SQ; ++role)
+        for (int b = 0; b < 2; ++b)
+            if (!p->roles[role][b].bound)
+                return fail(DP_ERR_UNBOUND, "role %s bank %d is not bound", names[role - DP_ROLE_MASTER], b);
+    dp_status s = need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
+    if (s == DP_OK) s = ensure_full(p);
+    if (s != DP_OK) return s;
+    s = single_pass_commit(p, stream);
+    if (s != DP_OK) return s;
+    p->buckets.clear();
+    p->bucket_elems = 0;
+    p->bucket_mode = 0;
     return DP_OK;
 }
 

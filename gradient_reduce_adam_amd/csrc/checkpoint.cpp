@@ -828,6 +828,7 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
     p->stats_current = false;
     p->buckets.clear();
     p->bucket_elems = 0;
+    p->bucket_mode = 0;
     return DP_OK;
 }
 

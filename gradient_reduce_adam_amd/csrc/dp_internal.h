@@ -114,9 +114,10 @@ hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateR
 // Single pass: the replica average of launch_reduce (same sources, order and
 // statistics) feeding the update of every element, from the current bank into
 // the other, with the scalars the step will have if it is applied (no clip).
-hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, const Srcs& accs,
-                               const Srcs& grads, const StateRefs& s, RoleRef p, StatsBuf sb, const DevState* st,
-                               const AdamArgs& args, hipStream_t stream);
+// Pieces [p0, p1) of the table: the whole table, or one bucket of it.
+hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, PieceSpan sp,
+                               const Srcs& accs, const Srcs& grads, const StateRefs& s, RoleRef p, StatsBuf sb,
+                               const DevState* st, const AdamArgs& args, hipStream_t stream);
 // After a skipped single-pass step: p = RNE(w) from the current bank again
 // (does nothing when the step was applied).
 hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& s, RoleRef p, const DevState* st,

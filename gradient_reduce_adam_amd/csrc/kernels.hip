@@ -766,9 +766,10 @@ hipError_t adamw_t(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& 
 }
 
 template <int kMode, int kGrad, int N>
-hipError_t reduce_adamw_n(dp_dtype pdt, const Table& t, const Srcs& accs, const Srcs& grads, const StateRefs& sr,
-                          RoleRef p, StatsBuf sb, const DevState* st, const AdamArgs& args, hipStream_t s) {
-    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+hipError_t reduce_adamw_n(dp_dtype pdt, const Table& t, PieceSpan sp, const Srcs& accs, const Srcs& grads,
+                          const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st, const AdamArgs& args,
+                          hipStream_t s) {
+    return for_span(sp.p0, sp.p1, 1, [&](int64_t b, dim3 grid) {
         if (pdt == DP_BF16)
             hipLaunchKernelGGL((k_reduce_adamw<kMode, kGrad, N, 2>), grid, dim3(kWave), 0, s, t, b, accs, grads, sr,
                                p, sb, st, args);
@@ -779,12 +780,12 @@ hipError_t reduce_adamw_n(dp_dtype pdt, const Table& t, const Srcs& accs, const 
 }
 
 template <int kMode, int kGrad>
-hipError_t reduce_adamw_dispatch(dp_dtype pdt, int n, const Table& t, const Srcs& accs, const Srcs& grads,
-                                 const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st,
+hipError_t reduce_adamw_dispatch(dp_dtype pdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,
+                                 const Srcs& grads, const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st,
                                  const AdamArgs& args, hipStream_t s) {
     switch (n) {
 #define DP_CASE(K) \
-    case K: return reduce_adamw_n<kMode, kGrad, K>(pdt, t, accs, grads, sr, p, sb, st, args, s);
+    case K: return reduce_adamw_n<kMode, kGrad, K>(pdt, t, sp, accs, grads, sr, p, sb, st, args, s);
         DP_CASE(1) DP_CASE(2) DP_CASE(3) DP_CASE(4) DP_CASE(5) DP_CASE(6) DP_CASE(7) DP_CASE(8)
         DP_CASE(9) DP_CASE(10) DP_CASE(11) DP_CASE(12) DP_CASE(13) DP_CASE(14) DP_CASE(15) DP_CASE(16)
 #undef DP_CASE
@@ -844,17 +845,18 @@ hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateR
     return t.flat ? adamw_t<true>(pdt, t, gbar, sr, p, st, args, s) : adamw_t<false>(pdt, t, gbar, sr, p, st, args, s);
 }
 
-hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, const Srcs& accs,
-                               const Srcs& grads, const StateRefs& sr, RoleRef p, StatsBuf sb, const DevState* st,
-                               const AdamArgs& args, hipStream_t s) {
-    if (t.flat) return hipErrorInvalidValue;  // statistics: table pieces
+hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, PieceSpan sp,
+                               const Srcs& accs, const Srcs& grads, const StateRefs& sr, RoleRef p, StatsBuf sb,
+                               const DevState* st, const AdamArgs& args, hipStream_t s) {
+    // statistics: table pieces, and a span inside the table
+    if (t.flat || sp.p0 < 0 || sp.p1 > t.npieces || sp.p0 > sp.p1) return hipErrorInvalidValue;
     if (mode == ReduceMode::kGradients) {
-        if (gdt == DP_F16) return reduce_adamw_dispatch<1, 1>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
-        return reduce_adamw_dispatch<1, 2>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+        if (gdt == DP_F16) return reduce_adamw_dispatch<1, 1>(pdt, n, t, sp, accs, grads, sr, p, sb, st, args, s);
+        return reduce_adamw_dispatch<1, 2>(pdt, n, t, sp, accs, grads, sr, p, sb, st, args, s);
     }
     if (mode == ReduceMode::kAccPlusGrad) {
-        if (gdt == DP_F16) return reduce_adamw_dispatch<2, 1>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
-        return reduce_adamw_dispatch<2, 2>(pdt, n, t, accs, grads, sr, p, sb, st, args, s);
+        if (gdt == DP_F16) return reduce_adamw_dispatch<2, 1>(pdt, n, t, sp, accs, grads, sr, p, sb, st, args, s);
+        return reduce_adamw_dispatch<2, 2>(pdt, n, t, sp, accs, grads, sr, p, sb, st, args, s);
     }
     return hipErrorInvalidValue;
 }

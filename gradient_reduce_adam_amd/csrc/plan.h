@@ -72,10 +72,15 @@ struct dp_plan {
     bool partials_valid = false;  // piece statistics of the current g_bar exist
     int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
     bool stats_current = false;   // dp_grad_stats ran on the current g_bar
-    // a reduction issued in buckets (dp_accumulate_reduce_range): the element
-    // ranges done so far, until they cover [0, P)
+    // a reduction issued in buckets: the element ranges done so far, until
+    // they cover [0, P).  bucket_mode 1: reduction buckets
+    // (dp_accumulate_reduce_range), complete once they cover [0, P); 2:
+    // single-pass buckets (dp_reduce_adam_range), with the update
+    // hyperparameters of the first one, complete at dp_reduce_adam_finish
     std::vector<std::pair<int64_t, int64_t>> buckets;
     int64_t bucket_elems = 0;
+    int bucket_mode = 0;
+    dp_adam_hparams bucket_hp{};
 };
 
 namespace dpapi {

@@ -46,18 +46,30 @@ GradProducer = Callable[[int, int, int, float], int]
 RangeProducer = Callable[[int, int, int, int, int], None]
 
 
-def backward_buckets(numel: Sequence[int], bucket_bytes: int, elem_bytes: int = 2) -> List[Tuple[int, int]]:
+def backward_buckets(numel: Sequence[int], bucket_bytes: int, elem_bytes: int = 2,
+                     split: bool = False) -> List[Tuple[int, int]]:
     """Buckets for a reduction that overlaps the backward pass: runs of whole
     tensors taken from the last tensor back to the first (the order in which
     a backward pass finishes them), each closed once it holds at least
-    bucket_bytes of gradients.  Returned in that order."""
+    bucket_bytes of gradients.  Returned in that order.  With split, a tensor
+    larger than one bucket is cut into buckets of bucket_bytes rounded down to
+    a multiple of 256 elements, counted from its start (the buckets of a flat
+    shard whose gradients arrive from the exchange in pieces)."""
     offs = [0]
     for x in numel:
         offs.append(offs[-1] + int(x))
     out: List[Tuple[int, int]] = []
     hi = offs[-1]
     acc = 0
+    step = max(256, (bucket_bytes // elem_bytes) // 256 * 256)
     for t in range(len(numel) - 1, -1, -1):
+        if split and int(numel[t]) * elem_bytes > bucket_bytes:
+            if offs[t + 1] < hi:  # close the run of smaller tensors after it
+                out.append((offs[t + 1], hi))
+            starts = list(range(offs[t], offs[t + 1], step))
+            out.extend(reversed(list(zip(starts, starts[1:] + [offs[t + 1]]))))
+            hi, acc = offs[t], 0
+            continue
         acc += int(numel[t]) * elem_bytes
         if acc >= bucket_bytes or t == 0:
             if offs[t] < hi:
@@ -310,9 +322,11 @@ class DPStep:
                         marks: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> Optional[dict]:
         """One step in which the backward pass of the last micro-step hands
         over its gradients bucket by bucket and the replica reduction follows
-        bucket by bucket (``dp_accumulate_reduce_range``); the earlier
-        micro-steps accumulate without any exchange, as a data-parallel run
-        with gradient accumulation does.
+        bucket by bucket (``dp_accumulate_reduce_range``); with
+        ``single_pass`` each bucket's reduction also updates its parameters
+        (``dp_reduce_adam_range``, then ``dp_reduce_adam_finish``).  The
+        earlier micro-steps accumulate without any exchange, as a
+        data-parallel run with gradient accumulation does.
 
         The gradient buffers are flat (grad_slots[r]: replica r's, P
         elements), and the producer fills them range by range on this step's
@@ -324,8 +338,6 @@ class DPStep:
         bits as ``step`` in either case.  marks, if given, are recorded on
         this step's stream before the last micro-step and after its last
         reduction."""
-        if self.single_pass:
-            raise ValueError("the bucketed reduction serves the two-pass update")
         pl, h = self.plan, self.plan.handle
         st = self.stream.cuda_stream
         self.steps_done += 1
@@ -345,14 +357,20 @@ class DPStep:
                 ev = torch.cuda.Event()
                 ev.record(self.stream)
                 rs.wait_event(ev)
-            pl.accumulate_reduce_range(lo, hi, stream=rs.cuda_stream)
+            if self.single_pass:
+                pl.reduce_adam_range(self.lr, self.eps, self.weight_decay, lo, hi, stream=rs.cuda_stream)
+            else:
+                pl.accumulate_reduce_range(lo, hi, stream=rs.cuda_stream)
         if rs is not self.stream:
             ev = torch.cuda.Event()
             ev.record(rs)
             self.stream.wait_event(ev)
         if marks is not None:
             marks[1].record(self.stream)
-        self.finish()
+        if self.single_pass:
+            pl.reduce_adam_finish(stream=st)
+        else:
+            self.finish()
         if sync_scale:
             state = self.read_state()
             self.scale = state["scale"]

@@ -323,6 +323,29 @@ dp_status dp_adam_step(dp_plan* plan, const dp_adam_hparams* hp, int64_t shard_b
  * step's statistics. */
 dp_status dp_reduce_adam_step(dp_plan* plan, const dp_adam_hparams* hp, hipStream_t stream);
 
+/* dp_reduce_adam_step in buckets: the single pass over one bucket [begin,
+ * end) of the flat space, so the update of the parameters whose gradients
+ * (or incoming partials) are complete can run while the backward pass, or
+ * the exchange, still produces the others (the bucketed overlap of the
+ * pages' data-parallel all-reduce, as for dp_accumulate_reduce_range).  The
+ * bucket rules are those of dp_accumulate_reduce_range: ends on the piece
+ * grid (DP_ERR_INVALID_ARG), no overlap (DP_ERR_STATE), any order, any
+ * streams.  Every bucket of one step takes the same hp (DP_ERR_INVALID_ARG
+ * otherwise).  Each bucket updates its elements into the other state bank
+ * with the scalars of an applied step and writes its statistics; nothing is
+ * committed until dp_reduce_adam_finish.  Until then every other step call
+ * returns DP_ERR_STATE. */
+dp_status dp_reduce_adam_range(dp_plan* plan, const dp_adam_hparams* hp, int64_t begin, int64_t end,
+                               hipStream_t stream);
+
+/* Completes a bucketed single pass once its buckets cover [0, P)
+ * (DP_ERR_STATE before): the statistics fold and the commit or skip of the
+ * step, with the parameters emitted again after a skip, exactly as at the
+ * end of dp_reduce_adam_step.  The result equals dp_reduce_adam_step bit
+ * for bit.  The caller orders this call after every bucket's launch, for
+ * example with events when the buckets ran on other streams. */
+dp_status dp_reduce_adam_finish(dp_plan* plan, hipStream_t stream);
+
 /* Copies the device scalar state into host struct out after the stream's
  * previous work (synchronises the stream). */
 dp_status dp_read_state(dp_plan* plan, dp_step_state* out, hipStream_t stream);

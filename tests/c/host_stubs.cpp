@@ -25,8 +25,9 @@ hipError_t launch_adamw(dp_dtype, const Table&, RoleRef, const StateRefs&, RoleR
                         hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_reduce_adamw(ReduceMode, dp_dtype, dp_dtype, int, const Table&, const Srcs&, const Srcs&,
-                               const StateRefs&, RoleRef, StatsBuf, const DevState*, const AdamArgs&, hipStream_t) {
+hipError_t launch_reduce_adamw(ReduceMode, dp_dtype, dp_dtype, int, const Table&, PieceSpan, const Srcs&,
+                               const Srcs&, const StateRefs&, RoleRef, StatsBuf, const DevState*, const AdamArgs&,
+                               hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_restore_param(dp_dtype, const Table&, const StateRefs&, RoleRef, const DevState*, hipStream_t) {

@@ -28,6 +28,31 @@ def test_backward_buckets_tile_the_space_in_reverse(mb):
                 assert 2 * (hi - off[t]) < bb
 
 
+@pytest.mark.parametrize("numel,mb", [((875000000,), 64), ((3000, 17, 70001, 256, 131075), 0.05),
+                                      ((5, 1 << 20, 7, 1 << 21, 3), 1), ((), 1), ((300, 0, 1000), 0.0001)])
+def test_split_backward_buckets_tile_on_the_piece_grid(numel, mb):
+    bb = int(mb * (1 << 20))
+    step = max(256, (bb // 2) // 256 * 256)
+    off = [0]
+    for x in numel:
+        off.append(off[-1] + x)
+    buckets = driver.backward_buckets(numel, bb, split=True)
+    if not numel or off[-1] == 0:
+        assert buckets == []
+        return
+    # contiguous, from the end of the flat space back to 0
+    assert buckets[0][1] == off[-1] and buckets[-1][0] == 0
+    for (lo, hi), (lo2, hi2) in zip(buckets, buckets[1:]):
+        assert hi2 == lo and lo2 < hi2
+    for lo, hi in buckets:
+        for x in (lo, hi):  # a tensor boundary, or a multiple of 256 into a tensor
+            t = max(i for i in range(len(numel)) if off[i] <= x) if x < off[-1] else len(numel)
+            assert x == off[-1] or x == off[t] or (x - off[t]) % 256 == 0
+        inside = [t for t in range(len(numel)) if off[t] <= lo < off[t + 1]]
+        if inside and numel[inside[0]] * 2 > bb:  # a cut of a large tensor
+            assert hi - lo <= step and hi <= off[inside[0] + 1]
+
+
 def test_backward_buckets_skip_empty_tensors():
     buckets = driver.backward_buckets((0, 5, 0, 0, 7, 0), 1)
     assert buckets == [(5, 12), (0, 5)]

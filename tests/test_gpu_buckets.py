@@ -2,7 +2,10 @@
 micro-step reduced bucket by bucket, on a second stream while the producer
 writes the next bucket, in backward order or shuffled, with buckets that
 split tensors.  It must give the same bits as the whole-range reduction, and
-so agree with the oracle; the ordering rules fail loudly."""
+so agree with the oracle; the ordering rules fail loudly.  The same for the
+bucketed single pass (dp_reduce_adam_range, then dp_reduce_adam_finish),
+whose buckets also update their parameters, against the whole-range single
+pass, skipped steps included."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +38,8 @@ def _split_inside(buckets, w):
     return out
 
 
-def _bucketed_run(w, steps, buckets, two_streams):
-    run = GpuRun(w)
+def _bucketed_run(w, steps, buckets, two_streams, single=False):
+    run = GpuRun(w, single_pass=single)
     d = run.d
     slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
     addrs = [t.data_ptr() for t in slots]
@@ -54,8 +57,8 @@ def _bucketed_run(w, steps, buckets, two_streams):
         del slots
 
 
-def _whole_run(w, steps):
-    run = GpuRun(w)
+def _whole_run(w, steps, single=False):
+    run = GpuRun(w, single_pass=single)
     try:
         states = run.run(steps)
         return run.window(0, w.P), states
@@ -65,7 +68,8 @@ def _whole_run(w, steps):
 
 def _same(a, b):
     (wa, sa), (wb, sb) = a, b
-    for k in ("w", "m", "v", "p", "gbar"):
+    assert wa.keys() == wb.keys()
+    for k in wa:
         assert np.array_equal(wa[k].view(np.uint8), wb[k].view(np.uint8)), k
     for x, y in zip(sa, sb):
         assert np.array_equal(np.array(list(x.values()), np.float64).view(np.uint64),
@@ -137,5 +141,81 @@ def test_bucket_ordering_errors():
         pl.grad_stats(False, 0.0, stream=s)
         pl.adam_step(w.lr, w.eps, w.weight_decay, stream=s)
         assert pl.read_state(stream=s)["t"] == 1
+    finally:
+        run.close()
+
+
+SINGLE_CASES = {
+    # ZeRO-style partials, dynamic scale that grows, an inf that skips step 2
+    "partials_dynamic_skip": dict(base="zero3_rank_7b", numel=RAGGED, n=4, a=1, growth_interval=2, steps=4,
+                                  injections=((2, 1, 1, 70000, float("inf")),)),
+    "n3_a2": dict(base="tiny", numel=RAGGED, n=3, a=2, steps=3),
+    "n1_a3": dict(base="unsharded_7b", numel=RAGGED, n=1, a=3, steps=2),
+}
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("name", sorted(SINGLE_CASES))
+def test_bucketed_single_pass_equals_whole_bitwise(name, two_streams):
+    spec = dict(SINGLE_CASES[name])
+    base = workloads.by_name(spec.pop("base"))
+    steps = spec.pop("steps")
+    w = base.with_(**spec)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 64 << 10), w)
+    log(f"single-pass buckets {name} two_streams={two_streams}: {len(buckets)} buckets")
+    got = _bucketed_run(w, steps, buckets, two_streams, single=True)
+    _same(got, _whole_run(w, steps, single=True))
+    if two_streams:
+        ref = oracle_run(w, steps)
+        for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
+            assert_scalars_match(g, r, where=f"{name} step {s}")
+        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+
+
+def test_shuffled_single_pass_buckets_equal_whole_bitwise():
+    w = workloads.tiny().with_(numel=RAGGED, n=2, a=2)
+    rng = np.random.default_rng(11)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 16 << 10), w)
+    buckets = [buckets[i] for i in rng.permutation(len(buckets))]
+    _same(_bucketed_run(w, 3, buckets, True, single=True), _whole_run(w, 3, single=True))
+
+
+def test_single_pass_bucket_ordering_errors():
+    w = workloads.tiny().with_(numel=(5000, 3000, 700), n=2, a=1)
+    run = GpuRun(w, single_pass=True)
+    pl, s = run.d.plan, run.stream
+    lr, eps, wd = w.lr, w.eps, w.weight_decay
+    try:
+        for r in range(w.n):
+            run.slots[r].zero_()
+            pl.bind("grad", run.slots[r], r)
+        with pytest.raises(dp.DpError) as e:  # nothing done yet
+            pl.reduce_adam_finish(stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        pl.reduce_adam_range(lr, eps, wd, 5000, 8000, stream=s)
+        with pytest.raises(dp.DpError) as e:  # other hyperparameters in the same step
+            pl.reduce_adam_range(2 * lr, eps, wd, 0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:  # overlap
+            pl.reduce_adam_range(lr, eps, wd, 5256, 8700, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:  # the other kind of bucket
+            pl.accumulate_reduce_range(0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        for call in (lambda: pl.reduce_adam_step(lr, eps, wd, stream=s), lambda: pl.grad_stats(False, 0.0, stream=s),
+                     lambda: pl.accumulate_all(True, stream=s), lambda: pl.accumulate_reduce(stream=s)):
+            with pytest.raises(dp.DpError) as e:
+                call()
+            assert e.value.status == dp.DP_ERR_STATE and "single pass" in e.value.message
+        with pytest.raises(dp.DpError) as e:  # 3000 + 700 of 8700 elements missing
+            pl.reduce_adam_finish(stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        pl.reduce_adam_range(lr, eps, wd, 8000, 8700, stream=s)
+        pl.reduce_adam_range(lr, eps, wd, 0, 5000, stream=s)
+        pl.reduce_adam_finish(stream=s)
+        st = pl.read_state(stream=s)
+        assert st["t"] == 1 and st["bank"] == 1
+        pl.reduce_adam_step(lr, eps, wd, stream=s)  # a whole-range step works again
+        assert pl.read_state(stream=s)["t"] == 2
     finally:
         run.close()
