@@ -460,6 +460,8 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
             reds.append(timed(lambda: d.plan.accumulate_reduce(stream=st), 1))
     t_red = sum(reds) / len(reds)
     d.close()
+    del d
+    torch.cuda.empty_cache()
     rs = torch.cuda.Stream()
     lines = []
     for mb in bucket_mbs:
@@ -487,6 +489,8 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
             res[mode] = timed(step, steps)
             last_ms[mode] = sum(a.elapsed_time(b) for a, b in marks) / len(marks)
             d.close()
+            del d
+            torch.cuda.empty_cache()
         saved = last_ms["sequential"] - last_ms["overlapped"]
         what = "replica reduction and update" if single else "replica reduction"
         lines.append({"metric": f"last micro-step (synthetic backward + {what}) with the {what} "

@@ -438,4 +438,11 @@ class DPStep:
         return self.banks[self.read_state()["bank"]]
 
     def close(self) -> None:
+        """Destroys the plan and drops this step's arrays, so their memory
+        returns to torch's allocator unless the caller still holds them."""
         self.plan.close()
+        self.master = self.exp_avg = self.exp_avg_sq = self.param = self.gbar = None
+        self.banks, self.acc = [], []
+        for name in ("arena", "stage"):
+            if hasattr(self, name):
+                setattr(self, name, None)
