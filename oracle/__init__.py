@@ -221,13 +221,15 @@ def _step_chunk(w, step: int, lo: int, hi: int, scale: float, grad_fn: GradFn):
 
 
 def run(w, steps: int, grad_fn: GradFn, master_fn: MasterFn, windows: Optional[Sequence[Tuple[int, int]]] = None,
-        threads: int = 8, chunk: int = 1 << 20, keep_gbar: Sequence[int] = ()) -> RunResult:
+        threads: int = 8, chunk: int = 1 << 20, keep_gbar: Sequence[int] = (),
+        progress: Optional[Callable[[int, dict], None]] = None) -> RunResult:
     """Runs ``steps`` data-parallel steps of workload ``w`` and returns the
     state on ``windows`` (default: the whole flat range).
 
     The global statistics always cover the whole flat range [0, P); the
     update is applied on the windows only (each element's update depends on
-    the global scalars and its own values alone)."""
+    the global scalars and its own values alone).  ``progress(step,
+    scalars)``, if given, is called after each step (reporting only)."""
     P = w.P
     windows = [(0, P)] if windows is None else [tuple(x) for x in windows]
     st = ScalarState(w.beta1, w.beta2, w.scaler, w.init_scale, w.backoff, w.growth, w.growth_interval)
@@ -272,4 +274,6 @@ def run(w, steps: int, grad_fn: GradFn, master_fn: MasterFn, windows: Optional[S
         for win in windows:
             S = res.state[win]
             adamw(S["w"], S["m"], S["v"], S["p"], w.param_dtype, wgbar[win], st, w.lr, w.eps, w.weight_decay)
+        if progress is not None:
+            progress(s, rec)
     return res

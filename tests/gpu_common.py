@@ -90,7 +90,7 @@ class GpuRun:
 # ----------------------------------------------------------------------------
 # oracle side
 # ----------------------------------------------------------------------------
-def oracle_run(w, steps: int, windows=None, keep_gbar=(), chunk: int = 1 << 20):
+def oracle_run(w, steps: int, windows=None, keep_gbar=(), chunk: int = 1 << 20, progress=None):
     def grad_fn(step, r, k, lo, hi, scale):
         return synth.grad_host(w, step, r, k, lo, hi, scale)
 
@@ -98,7 +98,7 @@ def oracle_run(w, steps: int, windows=None, keep_gbar=(), chunk: int = 1 << 20):
         return synth.master_host(w, lo, hi)
 
     return oracle.run(w, steps, grad_fn, master_fn, windows=windows, threads=THREADS, chunk=chunk,
-                      keep_gbar=keep_gbar)
+                      keep_gbar=keep_gbar, progress=progress)
 
 
 # ----------------------------------------------------------------------------
