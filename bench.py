@@ -69,6 +69,9 @@ def parse():
                          "4 flops per parameter and token, then the gradients) with the last micro-step's "
                          "reduction in buckets of these sizes, sequential and overlapped on a second stream; "
                          "one JSON line per bucket size")
+    ap.add_argument("--micro-buckets", action="store_true",
+                    help="with --overlap: the earlier micro-steps are also accumulated bucket by bucket as the "
+                         "backward pass produces them (dp_accumulate_all_range), overlapped in the same way")
     ap.add_argument("--tokens", type=int, default=4096, help="tokens per micro-batch of the synthetic backward")
     ap.add_argument("--log-steps", default="", metavar="FILE",
                     help="after everything timed, run --steps more steps, each followed by a read of the scalar "
@@ -412,10 +415,11 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     return elapsed, per_kind, state, ckpt, used_layout
 
 
-def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: bool = False):
+def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: bool = False, micro: bool = False):
     """The bucketed reduction overlapped with a synthetic backward pass; with
     single, each bucket's reduction also updates its parameters (the single
-    pass in buckets)."""
+    pass in buckets); with micro, the earlier micro-steps' accumulation is
+    bucketed and overlapped too."""
     import torch
 
     import synth
@@ -481,7 +485,7 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
                 m = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 marks.append(m)
                 d.step_overlapped(addrs, produce, buckets, reduce_stream=rs if mode == "overlapped" else None,
-                                  sync_scale=False, marks=m)
+                                  sync_scale=False, marks=m, micro_buckets=micro)
 
             for _ in range(warmup):
                 step()
@@ -497,7 +501,8 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
                                 "in buckets, sequential and overlapped on a second stream", "unit": "ms",
                       "config": {"workload": w.name, "bucket_mb": mb, "buckets": len(buckets), "tokens": tokens,
                                  "buckets_cut_tensors": bool(w.partials),
-                                 "update": "single-pass" if single else "two-pass"},
+                                 "update": "single-pass" if single else "two-pass",
+                                 "micro_steps_bucketed": bool(micro)},
                       "last_micro_step_sequential_ms": last_ms["sequential"],
                       "last_micro_step_overlapped_ms": last_ms["overlapped"], "saved_ms": saved,
                       "step_sequential_ms": res["sequential"], "step_overlapped_ms": res["overlapped"],
@@ -600,7 +605,7 @@ def main():
     single = single_pass_for(w, args.update)
     if args.overlap:
         for line in run_overlap(w, args.steps, args.warmup, [float(x) for x in args.overlap.split(",")],
-                                args.tokens, single):
+                                args.tokens, single, args.micro_buckets):
             print(json.dumps(line), flush=True)
         return
     elapsed, per_kind, state, ckpt, layout = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,

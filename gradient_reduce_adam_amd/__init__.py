@@ -39,8 +39,8 @@ ROLES = {"param": DP_ROLE_PARAM, "master": DP_ROLE_MASTER, "exp_avg": DP_ROLE_EX
 # every exported symbol of dpstep.h
 EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_create", "dp_plan_destroy",
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
-           "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all", "dp_accumulate_reduce",
-           "dp_accumulate_reduce_range",
+           "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all",
+           "dp_accumulate_all_range", "dp_accumulate_reduce", "dp_accumulate_reduce_range",
            "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_range",
            "dp_reduce_adam_finish", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
@@ -148,6 +148,7 @@ def _load():
         "dp_state_init": (ctypes.c_int, [vp, ctypes.POINTER(StateCfg), vp]),
         "dp_accumulate": (ctypes.c_int, [vp, i32, i32, i32, vp]),
         "dp_accumulate_all": (ctypes.c_int, [vp, i32, vp]),
+        "dp_accumulate_all_range": (ctypes.c_int, [vp, i32, i64, i64, vp]),
         "dp_accumulate_reduce": (ctypes.c_int, [vp, vp]),
         "dp_accumulate_reduce_range": (ctypes.c_int, [vp, i64, i64, vp]),
         "dp_reduce_replicas": (ctypes.c_int, [vp, ctypes.c_int, vp]),
@@ -274,6 +275,11 @@ def dp_accumulate(plan: int, replica: int, first: bool, emit_stats: bool = False
 
 def dp_accumulate_all(plan: int, first: bool, stream=None) -> None:
     _check(lib.dp_accumulate_all(ctypes.c_void_p(plan), int(bool(first)), ctypes.c_void_p(_stream(stream))))
+
+
+def dp_accumulate_all_range(plan: int, first: bool, begin: int, end: int, stream=None) -> None:
+    _check(lib.dp_accumulate_all_range(ctypes.c_void_p(plan), int(bool(first)), begin, end,
+                                       ctypes.c_void_p(_stream(stream))))
 
 
 def dp_accumulate_reduce(plan: int, stream=None) -> None:
@@ -461,6 +467,9 @@ class Plan:
 
     def accumulate_all(self, first: bool, stream=None) -> None:
         dp_accumulate_all(self.handle, first, stream)
+
+    def accumulate_all_range(self, first: bool, begin: int, end: int, stream=None) -> None:
+        dp_accumulate_all_range(self.handle, first, begin, end, stream)
 
     def accumulate_reduce(self, stream=None) -> None:
         dp_accumulate_reduce(self.handle, stream)

@@ -191,14 +191,35 @@ bool all_flat(const dpk::StateRefs& s) {
     return true;
 }
 
-// Calls that start or end a reduction may not run while a bucketed one is
-// half done.
-dp_status no_open_buckets(const dp_plan* p, const char* where) {
-    if (!p->buckets.empty())
+const char* bucket_kind(int mode) {
+    switch (mode) {
+        case 1: return "reduction (dp_accumulate_reduce_range)";
+        case 2: return "single pass (dp_reduce_adam_range, then dp_reduce_adam_finish)";
+        case 3: return "micro-step (dp_accumulate_all_range)";
+    }
+    return "call";
+}
+
+// Calls on whole accumulators or on g_bar may not run while a bucketed call
+// is half done; a bucketed call may not start while buckets of another kind
+// are open (mode: the caller's kind, 0 for a whole-space call).
+dp_status no_open_buckets(const dp_plan* p, const char* where, int mode = 0) {
+    if (!p->buckets.empty() && p->bucket_mode != mode)
         return fail(DP_ERR_STATE, "%s while a bucketed %s covers %lld of %lld elements", where,
-                    p->bucket_mode == 2 ? "single pass (dp_reduce_adam_range, then dp_reduce_adam_finish)"
-                                        : "reduction",
-                    static_cast<long long>(p->bucket_elems), static_cast<long long>(p->P));
+                    bucket_kind(p->bucket_mode), static_cast<long long>(p->bucket_elems),
+                    static_cast<long long>(p->P));
+    return DP_OK;
+}
+
+// Replicas must be at the same micro-step; with first == 0, past the first.
+dp_status same_micro_step(const dp_plan* p, bool first) {
+    for (int32_t r = 0; r < p->n; ++r) {
+        if (!first && p->micro[r] == 0)
+            return fail(DP_ERR_STATE, "replica %d: first == 0 without a first micro-step since the last reduction", r);
+        if (p->micro[r] != p->micro[0])
+            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
+                        p->micro[r], p->micro[0]);
+    }
     return DP_OK;
 }
 
@@ -610,13 +631,8 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     dp_status s = bound_replicas(p, DP_ROLE_GRAD, &grads);
     if (s == DP_OK) s = bound_replicas(p, DP_ROLE_ACC, &accs);
     if (s != DP_OK) return s;
-    for (int32_t r = 0; r < p->n; ++r) {
-        if (!first && p->micro[r] == 0)
-            return fail(DP_ERR_STATE, "replica %d: first == 0 without a first micro-step since the last reduction", r);
-        if (p->micro[r] != p->micro[0])
-            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
-                        p->micro[r], p->micro[0]);
-    }
+    s = same_micro_step(p, first != 0);
+    if (s != DP_OK) return s;
     s = ensure_full(p);
     if (s != DP_OK) return s;
     // Addressing (flat pieces or chunk-table pieces, see kernels.hip), as
@@ -629,7 +645,8 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     // statistics does not depend on how the roles are bound.
     const dpk::Table t = p->full.table(first && all_flat(grads, p->n) && all_flat(accs, p->n));
     if (t.npieces > 0) {
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, grads, accs, stream),
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, dpk::PieceSpan{0, t.npieces}, grads,
+                                                    accs, stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
@@ -639,12 +656,53 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     return DP_OK;
 }
 
+dp_status dp_accumulate_all_range(dp_plan* p, int32_t first, int64_t begin, int64_t end, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_all_range: null plan");
+    dp_status s = no_open_buckets(p, "dp_accumulate_all_range", 3);
+    if (s != DP_OK) return s;
+    if (p->bucket_mode == 3 && !p->buckets.empty() && (first != 0) != (p->bucket_first != 0))
+        return fail(DP_ERR_INVALID_ARG, "the buckets of one micro-step take the same first flag (%d here, %d before)",
+                    first != 0, p->bucket_first != 0);
+    dpk::Srcs grads{}, accs{};
+    s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+    if (s == DP_OK) s = bound_replicas(p, DP_ROLE_ACC, &accs);
+    if (s != DP_OK) return s;
+    s = same_micro_step(p, first != 0);
+    if (s != DP_OK) return s;
+    int64_t p0 = 0, p1 = 0;
+    s = bucket_span(p, begin, end, &p0, &p1);
+    if (s != DP_OK) return s;
+    // table pieces, as every read-modify-write micro-step uses; the adds are
+    // elementwise, so the pieces a bucket is cut into never change the bits
+    if (p1 > p0) {
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.table(false),
+                                                    dpk::PieceSpan{p0, p1}, grads, accs, stream),
+                         "accumulate launch");
+        if (s != DP_OK) return s;
+    }
+    if (end > begin) {
+        if (p->buckets.empty()) p->bucket_first = first != 0;
+        p->buckets.emplace_back(begin, end);
+        p->bucket_elems += end - begin;
+        p->bucket_mode = 3;
+    }
+    p->stats_current = false;
+    p->partials_valid = false;
+    if (p->bucket_elems == p->P) {  // the buckets cover [0, P): the micro-step is complete
+        p->buckets.clear();
+        p->bucket_elems = 0;
+        p->bucket_mode = 0;
+        for (int32_t r = 0; r < p->n; ++r) p->micro[r] = first ? 1 : p->micro[r] + 1;
+    }
+    return DP_OK;
+}
+
 dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce_range: null plan");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce_range before dp_state_init");
-    if (p->bucket_mode == 2 && !p->buckets.empty())
-        return fail(DP_ERR_STATE, "dp_accumulate_reduce_range while a bucketed single pass is open");
-    dp_status s = bucket_span(p, begin, end, nullptr, nullptr);
+    dp_status s = no_open_buckets(p, "dp_accumulate_reduce_range", 1);
+    if (s != DP_OK) return s;
+    s = bucket_span(p, begin, end, nullptr, nullptr);
     if (s != DP_OK) return s;
     const int64_t p0 = piece_at(p, begin), p1 = piece_at(p, end);
     const Binding* gb = gbar_binding(p);
@@ -856,8 +914,10 @@ dp_status dp_reduce_adam_range(dp_plan* p, const dp_adam_hparams* hp, int64_t be
     if (!p || !hp) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_range: null argument");
     if (!valid_hparams(hp)) return fail(DP_ERR_INVALID_ARG, "need lr >= 0, eps > 0, weight_decay >= 0");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_range before dp_state_init");
-    if (p->bucket_mode == 1 && !p->buckets.empty())
-        return fail(DP_ERR_STATE, "dp_reduce_adam_range while a bucketed reduction is half done");
+    {
+        dp_status g = no_open_buckets(p, "dp_reduce_adam_range", 2);
+        if (g != DP_OK) return g;
+    }
     if (p->bucket_mode == 2 && !p->buckets.empty()) {
         const dp_adam_hparams& h = p->bucket_hp;
         if (h.lr != hp->lr || h.eps != hp->eps || h.weight_decay != hp->weight_decay)
@@ -886,8 +946,10 @@ dp_status dp_reduce_adam_range(dp_plan* p, const dp_adam_hparams* hp, int64_t be
 dp_status dp_reduce_adam_finish(dp_plan* p, hipStream_t stream) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_adam_finish: null plan");
     if (!p->state_ready) return fail(DP_ERR_STATE, "dp_reduce_adam_finish before dp_state_init");
-    if (p->bucket_mode == 1 && !p->buckets.empty())
-        return fail(DP_ERR_STATE, "dp_reduce_adam_finish while a bucketed reduction is half done");
+    {
+        dp_status g = no_open_buckets(p, "dp_reduce_adam_finish", 2);
+        if (g != DP_OK) return g;
+    }
     if (p->bucket_elems != p->P)
         return fail(DP_ERR_STATE, "dp_reduce_adam_finish: the buckets cover %lld of %lld elements",
                     static_cast<long long>(p->bucket_elems), static_cast<long long>(p->P));

@@ -91,8 +91,6 @@ struct StateRefs {
 
 hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& t, RoleRef grad, RoleRef acc,
                              StatsBuf sb, hipStream_t stream);
-hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
-                                 hipStream_t stream);
 
 // What each replica contributes to the reduction.
 enum class ReduceMode {
@@ -104,6 +102,10 @@ enum class ReduceMode {
 struct PieceSpan {
     int64_t p0, p1;
 };
+// Every replica's micro-step over pieces [p0, p1) of the table (flat pieces
+// only for the first micro-step).
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, PieceSpan sp, const Srcs& grads,
+                                 const Srcs& accs, hipStream_t stream);
 hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,
                          const Srcs& grads, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t stream);

@@ -738,9 +738,9 @@ hipError_t accumulate_t(dp_dtype gdt, bool first, bool stats, const Table& t, Ro
 }
 
 template <bool kFlat>
-hipError_t accumulate_all_t(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
-                            hipStream_t s) {
-    return for_pieces(t.npieces, static_cast<unsigned>(n), [&](int64_t b, dim3 grid) {
+hipError_t accumulate_all_t(dp_dtype gdt, bool first, int n, const Table& t, PieceSpan sp, const Srcs& grads,
+                            const Srcs& accs, hipStream_t s) {
+    return for_span(sp.p0, sp.p1, static_cast<unsigned>(n), [&](int64_t b, dim3 grid) {
         const dim3 blk(kWave);
 #define DP_ALL(G, F) hipLaunchKernelGGL((k_accumulate_all<kFlat, G, F>), grid, blk, 0, s, t, b, grads, accs)
         if constexpr (kFlat) {
@@ -804,11 +804,11 @@ hipError_t launch_accumulate(dp_dtype gdt, bool first, bool stats, const Table& 
                   : accumulate_t<false>(gdt, first, stats, t, grad, acc, sb, s);
 }
 
-hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, const Srcs& grads, const Srcs& accs,
-                                 hipStream_t s) {
-    if (t.flat && !first) return hipErrorInvalidValue;
-    return t.flat ? accumulate_all_t<true>(gdt, true, n, t, grads, accs, s)
-                  : accumulate_all_t<false>(gdt, first, n, t, grads, accs, s);
+hipError_t launch_accumulate_all(dp_dtype gdt, bool first, int n, const Table& t, PieceSpan sp, const Srcs& grads,
+                                 const Srcs& accs, hipStream_t s) {
+    if ((t.flat && !first) || sp.p0 < 0 || sp.p1 > t.npieces || sp.p0 > sp.p1) return hipErrorInvalidValue;
+    return t.flat ? accumulate_all_t<true>(gdt, true, n, t, sp, grads, accs, s)
+                  : accumulate_all_t<false>(gdt, first, n, t, sp, grads, accs, s);
 }
 
 hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, PieceSpan sp, const Srcs& accs,

@@ -72,15 +72,18 @@ struct dp_plan {
     bool partials_valid = false;  // piece statistics of the current g_bar exist
     int64_t partials_count = 0;   // how many (they follow the launch that wrote them)
     bool stats_current = false;   // dp_grad_stats ran on the current g_bar
-    // a reduction issued in buckets: the element ranges done so far, until
-    // they cover [0, P).  bucket_mode 1: reduction buckets
+    // a call issued in buckets: the element ranges done so far, until they
+    // cover [0, P).  bucket_mode 1: reduction buckets
     // (dp_accumulate_reduce_range), complete once they cover [0, P); 2:
     // single-pass buckets (dp_reduce_adam_range), with the update
-    // hyperparameters of the first one, complete at dp_reduce_adam_finish
+    // hyperparameters of the first one, complete at dp_reduce_adam_finish;
+    // 3: buckets of one micro-step of every replica (dp_accumulate_all_range),
+    // with the `first` flag of the first one, complete once they cover [0, P)
     std::vector<std::pair<int64_t, int64_t>> buckets;
     int64_t bucket_elems = 0;
     int bucket_mode = 0;
     dp_adam_hparams bucket_hp{};
+    int32_t bucket_first = 0;
 };
 
 namespace dpapi {

@@ -319,14 +319,17 @@ class DPStep:
 
     def step_overlapped(self, grad_slots: Sequence[int], produce: RangeProducer, buckets: Sequence[Tuple[int, int]],
                         reduce_stream: Optional[torch.cuda.Stream] = None, sync_scale: bool = True,
-                        marks: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None) -> Optional[dict]:
+                        marks: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
+                        micro_buckets: bool = False) -> Optional[dict]:
         """One step in which the backward pass of the last micro-step hands
         over its gradients bucket by bucket and the replica reduction follows
         bucket by bucket (``dp_accumulate_reduce_range``); with
         ``single_pass`` each bucket's reduction also updates its parameters
         (``dp_reduce_adam_range``, then ``dp_reduce_adam_finish``).  The
         earlier micro-steps accumulate without any exchange, as a
-        data-parallel run with gradient accumulation does.
+        data-parallel run with gradient accumulation does: over the whole
+        space after their backward pass, or with ``micro_buckets`` bucket by
+        bucket as it produces them (``dp_accumulate_all_range``).
 
         The gradient buffers are flat (grad_slots[r]: replica r's, P
         elements), and the producer fills them range by range on this step's
@@ -335,9 +338,11 @@ class DPStep:
         production of the next bucket (events order each bucket's reduction
         after its production, and the statistics after every reduction).
         Without one, production and reduction alternate on one stream.  Same
-        bits as ``step`` in either case.  marks, if given, are recorded on
-        this step's stream before the last micro-step and after its last
-        reduction."""
+        bits as ``step`` in either case.  With bucketed micro-steps on a
+        second stream, the producer rewrites a bucket of the gradient buffers
+        only after the previous micro-step's accumulation has read it (one
+        event per bucket).  marks, if given, are recorded on this step's
+        stream before the last micro-step and after its last reduction."""
         pl, h = self.plan, self.plan.handle
         st = self.stream.cuda_stream
         self.steps_done += 1
@@ -345,18 +350,36 @@ class DPStep:
         for r, addr in enumerate(grad_slots):
             dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr)
         last = 1 if self.partials else self.a
-        for k in range(1, last):
-            produce(s, k, 0, self.P, st)
-            pl.accumulate_all(first=(k == 1), stream=st)
-        if marks is not None:
-            marks[0].record(self.stream)
         rs = reduce_stream if reduce_stream is not None else self.stream
-        for lo, hi in buckets:
-            produce(s, last, lo, hi, st)
-            if rs is not self.stream:
+        two = rs is not self.stream
+        read = {}  # bucket -> event on rs after the last launch that read its gradients
+
+        def produce_bucket(k, i, lo, hi):
+            # the producer rewrites bucket i once its previous contents are
+            # read, and the consumer reads it once it is written
+            if two and i in read:
+                self.stream.wait_event(read[i])
+            produce(s, k, lo, hi, st)
+            if two:
                 ev = torch.cuda.Event()
                 ev.record(self.stream)
                 rs.wait_event(ev)
+
+        for k in range(1, last):
+            if micro_buckets:
+                for i, (lo, hi) in enumerate(buckets):
+                    produce_bucket(k, i, lo, hi)
+                    pl.accumulate_all_range(k == 1, lo, hi, stream=rs.cuda_stream)
+                    if two:
+                        read[i] = torch.cuda.Event()
+                        read[i].record(rs)
+            else:
+                produce(s, k, 0, self.P, st)
+                pl.accumulate_all(first=(k == 1), stream=st)
+        if marks is not None:
+            marks[0].record(self.stream)
+        for i, (lo, hi) in enumerate(buckets):
+            produce_bucket(last, i, lo, hi)
             if self.single_pass:
                 pl.reduce_adam_range(self.lr, self.eps, self.weight_decay, lo, hi, stream=rs.cuda_stream)
             else:

@@ -235,6 +235,22 @@ dp_status dp_accumulate(dp_plan* plan, int32_t replica, int32_t first, int32_t e
  * micro-step. */
 dp_status dp_accumulate_all(dp_plan* plan, int32_t first, hipStream_t stream);
 
+/* dp_accumulate_all over one bucket [begin, end) of the flat space, so each
+ * micro-step's accumulation can follow its backward pass bucket by bucket and
+ * a bucket's gradient buffer is free for reuse as soon as it is added in [first
+ * page, averaging formula paragraph: the a micro-steps of each device are
+ * summed before the exchange].  The bucket rules are those of
+ * dp_accumulate_reduce_range: each end a tensor start, P, or a multiple of 256
+ * elements into its tensor (DP_ERR_INVALID_ARG); the buckets of one
+ * micro-step come in any order and on several streams, do not overlap
+ * (DP_ERR_STATE) and take the same first flag (DP_ERR_INVALID_ARG).  Once they
+ * cover [0, P) the micro-step is complete and the accumulators hold, bit for
+ * bit, what dp_accumulate_all(first) leaves.  Until then every other
+ * accumulation, reduction, statistics or single-pass call returns
+ * DP_ERR_STATE.  DP_ERR_STATE as for dp_accumulate_all for the micro-step
+ * counts. */
+dp_status dp_accumulate_all_range(dp_plan* plan, int32_t first, int64_t begin, int64_t end, hipStream_t stream);
+
 /* The last micro-step fused with the replica average: GBAR = (sum_r
  * (ACC[r] + GRAD[r])) / n in the order of dp_reduce_replicas, plus the
  * per-chunk statistics; bit for bit the result of dp_accumulate on every

@@ -10,7 +10,7 @@ namespace dpk {
 hipError_t launch_accumulate(dp_dtype, bool, bool, const Table&, RoleRef, RoleRef, StatsBuf, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_accumulate_all(dp_dtype, bool, int, const Table&, const Srcs&, const Srcs&, hipStream_t) {
+hipError_t launch_accumulate_all(dp_dtype, bool, int, const Table&, PieceSpan, const Srcs&, const Srcs&, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_reduce(ReduceMode, dp_dtype, int, const Table&, PieceSpan, const Srcs&, const Srcs&, RoleRef,

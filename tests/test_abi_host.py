@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     assert sorted(dp.EXPORTS) == names
     for n in names:
         assert hasattr(dp.lib, n), n
@@ -202,6 +202,24 @@ def test_bind_and_call_errors_before_any_launch():
             dp.dp_plan_chunks(h, 0, 2000)
         assert e.value.status == dp.DP_ERR_RANGE
         assert "not inside" in dp.dp_last_error()
+
+
+def test_ranged_micro_step_errors_before_any_launch():
+    with dp.Plan((1000, 24), 2, "bf16", "bf16") as p:
+        h = p.handle
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate_all_range(h, True, 0, 256, stream=0)  # nothing bound
+        assert e.value.status == dp.DP_ERR_UNBOUND
+        for r in range(2):
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_GRAD, r, 0x1000 * (r + 1))
+            dp.dp_plan_bind_flat(h, dp.DP_ROLE_ACC, r, 0x10000 * (r + 1))
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_accumulate_all_range(h, False, 0, 256, stream=0)  # no first micro-step yet
+        assert e.value.status == dp.DP_ERR_STATE
+        for b, e_ in ((-1, 256), (512, 256), (0, 1025)):
+            with pytest.raises(dp.DpError) as e:
+                dp.dp_accumulate_all_range(h, True, b, e_, stream=0)
+            assert e.value.status == dp.DP_ERR_RANGE
 
 
 def test_destroy_null_is_ok():

@@ -5,7 +5,8 @@ split tensors.  It must give the same bits as the whole-range reduction, and
 so agree with the oracle; the ordering rules fail loudly.  The same for the
 bucketed single pass (dp_reduce_adam_range, then dp_reduce_adam_finish),
 whose buckets also update their parameters, against the whole-range single
-pass, skipped steps included."""
+pass, skipped steps included; and for the earlier micro-steps accumulated
+bucket by bucket (dp_accumulate_all_range)."""
 import numpy as np
 import pytest
 import torch
@@ -38,7 +39,7 @@ def _split_inside(buckets, w):
     return out
 
 
-def _bucketed_run(w, steps, buckets, two_streams, single=False):
+def _bucketed_run(w, steps, buckets, two_streams, single=False, micro=False):
     run = GpuRun(w, single_pass=single)
     d = run.d
     slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
@@ -50,7 +51,8 @@ def _bucketed_run(w, steps, buckets, two_streams, single=False):
 
     rs = torch.cuda.Stream() if two_streams else None
     try:
-        states = [d.step_overlapped(addrs, produce, buckets, reduce_stream=rs) for _ in range(steps)]
+        states = [d.step_overlapped(addrs, produce, buckets, reduce_stream=rs, micro_buckets=micro)
+                  for _ in range(steps)]
         return run.window(0, w.P), states
     finally:
         run.close()
@@ -217,5 +219,88 @@ def test_single_pass_bucket_ordering_errors():
         assert st["t"] == 1 and st["bank"] == 1
         pl.reduce_adam_step(lr, eps, wd, stream=s)  # a whole-range step works again
         assert pl.read_state(stream=s)["t"] == 2
+    finally:
+        run.close()
+
+
+MICRO_CASES = {
+    "clip_n3_a2": (CASES["clip_n3_a2"], False),
+    "n1_a3": (CASES["n1_a3"], False),
+    "single_n3_a2": (SINGLE_CASES["n3_a2"], True),
+    "single_n1_a3": (SINGLE_CASES["n1_a3"], True),
+}
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("name", sorted(MICRO_CASES))
+def test_bucketed_micro_steps_equal_whole_bitwise(name, two_streams):
+    """Every micro-step accumulated bucket by bucket as the producer writes
+    it, the last one reduced (or reduced and applied) bucket by bucket: the
+    same bits as the whole-range step; on two streams the producer reuses the
+    gradient buffers while earlier buckets are still being added."""
+    spec, single = dict(MICRO_CASES[name][0]), MICRO_CASES[name][1]
+    base = workloads.by_name(spec.pop("base"))
+    steps = spec.pop("steps")
+    w = base.with_(**spec)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 64 << 10), w)
+    log(f"micro-step buckets {name} two_streams={two_streams}: {len(buckets)} buckets")
+    got = _bucketed_run(w, steps, buckets, two_streams, single=single, micro=True)
+    _same(got, _whole_run(w, steps, single=single))
+    if two_streams:
+        ref = oracle_run(w, steps)
+        for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
+            assert_scalars_match(g, r, where=f"{name} step {s}")
+        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+
+
+def test_shuffled_micro_step_buckets_equal_whole_bitwise():
+    w = workloads.gpt2_small().with_(numel=RAGGED, n=2, a=3, max_norm=0.05, scaled_tensors=(1,))
+    rng = np.random.default_rng(13)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 16 << 10), w)
+    buckets = [buckets[i] for i in rng.permutation(len(buckets))]
+    _same(_bucketed_run(w, 2, buckets, True, micro=True), _whole_run(w, 2))
+
+
+def test_micro_step_bucket_ordering_errors():
+    w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=3, scaled_tensors=())
+    run = GpuRun(w)
+    pl, s = run.d.plan, run.stream
+    try:
+        for r in range(w.n):
+            run.slots[r].zero_()
+            pl.bind("grad", run.slots[r], r)
+        with pytest.raises(dp.DpError) as e:  # no first micro-step yet
+            pl.accumulate_all_range(False, 0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        for lo, hi in ((3, 5000), (0, 4999)):  # ends off the piece grid
+            with pytest.raises(dp.DpError) as e:
+                pl.accumulate_all_range(True, lo, hi, stream=s)
+            assert e.value.status == dp.DP_ERR_INVALID_ARG
+        pl.accumulate_all_range(True, 5000, 8000, stream=s)
+        with pytest.raises(dp.DpError) as e:  # another first flag in the same micro-step
+            pl.accumulate_all_range(False, 0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:  # overlap
+            pl.accumulate_all_range(True, 5256, 8700, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:  # the other kinds of bucket
+            pl.accumulate_reduce_range(0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:
+            pl.reduce_adam_range(w.lr, w.eps, w.weight_decay, 0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        for call in (lambda: pl.accumulate_all(False, stream=s), lambda: pl.accumulate(0, True, stream=s),
+                     lambda: pl.accumulate_reduce(stream=s), lambda: pl.grad_stats(False, 0.0, stream=s),
+                     lambda: pl.reduce_replicas("acc", stream=s)):
+            with pytest.raises(dp.DpError) as e:  # the micro-step is half done
+                call()
+            assert e.value.status == dp.DP_ERR_STATE and "micro-step" in e.value.message
+        pl.accumulate_all_range(True, 0, 5000, stream=s)
+        pl.accumulate_all_range(True, 8000, 8700, stream=s)  # complete: micro-step 1
+        pl.accumulate_all_range(False, 0, 8700, stream=s)  # micro-step 2 as one bucket
+        pl.accumulate_reduce(stream=s)  # micro-step 3 fused with the reduction
+        pl.grad_stats(False, 0.0, stream=s)
+        pl.adam_step(w.lr, w.eps, w.weight_decay, stream=s)
+        assert pl.read_state(stream=s)["t"] == 1
     finally:
         run.close()
