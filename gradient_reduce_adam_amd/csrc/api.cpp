@@ -672,11 +672,19 @@ dp_status dp_accumulate_all_range(dp_plan* p, int32_t first, int64_t begin, int6
     int64_t p0 = 0, p1 = 0;
     s = bucket_span(p, begin, end, &p0, &p1);
     if (s != DP_OK) return s;
-    // table pieces, as every read-modify-write micro-step uses; the adds are
-    // elementwise, so the pieces a bucket is cut into never change the bits
+    // The addressing of dp_accumulate_all: flat pieces of [begin, end) for a
+    // first micro-step on flat bindings, else the bucket's span of table
+    // pieces.  The adds are elementwise, so the pieces a bucket is cut into
+    // never change the bits.
     if (p1 > p0) {
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, p->full.table(false),
-                                                    dpk::PieceSpan{p0, p1}, grads, accs, stream),
+        const bool flat = first && all_flat(grads, p->n) && all_flat(accs, p->n);
+        DeviceTable bucket;
+        bucket.begin = begin;
+        bucket.end = end;
+        bucket.log2s = p->full.log2s;
+        const dpk::Table t = flat ? bucket.table(true) : p->full.table(false);
+        const dpk::PieceSpan sp = flat ? dpk::PieceSpan{0, t.npieces} : dpk::PieceSpan{p0, p1};
+        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, sp, grads, accs, stream),
                          "accumulate launch");
         if (s != DP_OK) return s;
     }
