@@ -41,7 +41,7 @@ EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_creat
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all",
            "dp_accumulate_all_range", "dp_accumulate_reduce", "dp_accumulate_reduce_range",
-           "dp_reduce_replicas", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_range",
+           "dp_reduce_replicas", "dp_reduce_replicas_range", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_range",
            "dp_reduce_adam_finish", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
            "dp_checkpoint_load")
@@ -152,6 +152,7 @@ def _load():
         "dp_accumulate_reduce": (ctypes.c_int, [vp, vp]),
         "dp_accumulate_reduce_range": (ctypes.c_int, [vp, i64, i64, vp]),
         "dp_reduce_replicas": (ctypes.c_int, [vp, ctypes.c_int, vp]),
+        "dp_reduce_replicas_range": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp]),
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
         "dp_reduce_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), vp]),
@@ -292,6 +293,10 @@ def dp_accumulate_reduce_range(plan: int, begin: int, end: int, stream=None) -> 
 
 def dp_reduce_replicas(plan: int, src: int = DP_ROLE_ACC, stream=None) -> None:
     _check(lib.dp_reduce_replicas(ctypes.c_void_p(plan), src, ctypes.c_void_p(_stream(stream))))
+
+
+def dp_reduce_replicas_range(plan: int, src: int, begin: int, end: int, stream=None) -> None:
+    _check(lib.dp_reduce_replicas_range(ctypes.c_void_p(plan), src, begin, end, ctypes.c_void_p(_stream(stream))))
 
 
 def dp_grad_stats(plan: int, scan: bool, max_norm: float = 0.0, stream=None) -> None:
@@ -479,6 +484,9 @@ class Plan:
 
     def reduce_replicas(self, src: str = "acc", stream=None) -> None:
         dp_reduce_replicas(self.handle, ROLES[src], stream)
+
+    def reduce_replicas_range(self, src: str, begin: int, end: int, stream=None) -> None:
+        dp_reduce_replicas_range(self.handle, ROLES[src], begin, end, stream)
 
     def grad_stats(self, scan: bool = False, max_norm: float = 0.0, stream=None) -> None:
         dp_grad_stats(self.handle, scan, max_norm, stream)

@@ -193,7 +193,7 @@ bool all_flat(const dpk::StateRefs& s) {
 
 const char* bucket_kind(int mode) {
     switch (mode) {
-        case 1: return "reduction (dp_accumulate_reduce_range)";
+        case 1: return "reduction (dp_accumulate_reduce_range or dp_reduce_replicas_range)";
         case 2: return "single pass (dp_reduce_adam_range, then dp_reduce_adam_finish)";
         case 3: return "micro-step (dp_accumulate_all_range)";
     }
@@ -705,37 +705,54 @@ dp_status dp_accumulate_all_range(dp_plan* p, int32_t first, int64_t begin, int6
     return DP_OK;
 }
 
-dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hipStream_t stream) {
-    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce_range: null plan");
-    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_accumulate_reduce_range before dp_state_init");
-    dp_status s = no_open_buckets(p, "dp_accumulate_reduce_range", 1);
+// One bucket of a bucketed reduction from the given sources; every bucket of
+// one reduction takes the same kind (src: 0 the last micro-step fused, else
+// the role reduced alone).
+static dp_status reduction_bucket(dp_plan* p, int src, int64_t begin, int64_t end, hipStream_t stream,
+                                  const char* where) {
+    if (!p->state_ready) return fail(DP_ERR_STATE, "%s before dp_state_init", where);
+    dp_status s = no_open_buckets(p, where, 1);
     if (s != DP_OK) return s;
-    s = bucket_span(p, begin, end, nullptr, nullptr);
+    if (p->bucket_mode == 1 && !p->buckets.empty() && p->bucket_src != src)
+        return fail(DP_ERR_INVALID_ARG, "%s: the buckets of one reduction take the same sources", where);
+    int64_t p0 = 0, p1 = 0;
+    s = bucket_span(p, begin, end, &p0, &p1);
     if (s != DP_OK) return s;
-    const int64_t p0 = piece_at(p, begin), p1 = piece_at(p, end);
     const Binding* gb = gbar_binding(p);
     if (!gb->bound) return fail(DP_ERR_UNBOUND, "role GBAR is not bound");
     dpk::Srcs grads{}, accs{};
-    s = bound_replicas(p, DP_ROLE_GRAD, &grads);
-    if (s != DP_OK) return s;
-    for (int32_t r = 0; r < p->n; ++r)
-        if (p->micro[r] != p->micro[0])
-            return fail(DP_ERR_STATE, "replicas are at different micro-steps (replica %d: %d, replica 0: %d)", r,
-                        p->micro[r], p->micro[0]);
-    const bool with_acc = p->micro[0] > 0;
-    if (with_acc) {
+    dpk::ReduceMode mode = dpk::ReduceMode::kGradients;
+    if (src == DP_ROLE_ACC) {
         s = bound_replicas(p, DP_ROLE_ACC, &accs);
         if (s != DP_OK) return s;
+        for (int32_t r = 0; r < p->n; ++r)
+            if (p->micro[r] != p->micro[0] || p->micro[r] == 0)
+                return fail(DP_ERR_STATE,
+                            "replicas accumulated different numbers of micro-steps (replica %d: %d, replica 0: %d)", r,
+                            p->micro[r], p->micro[0]);
+        mode = dpk::ReduceMode::kAccumulators;
+    } else {
+        s = bound_replicas(p, DP_ROLE_GRAD, &grads);
+        if (s != DP_OK) return s;
+        if (src == 0) {
+            s = same_micro_step(p, true);
+            if (s != DP_OK) return s;
+            if (p->micro[0] > 0) {
+                s = bound_replicas(p, DP_ROLE_ACC, &accs);
+                if (s != DP_OK) return s;
+                mode = dpk::ReduceMode::kAccPlusGrad;
+            }
+        }
     }
     const dpk::Table t = p->full.table(false);  // statistics: table pieces, the slots of the whole reduction
     if (p1 > p0) {
-        s = check_launch(dpk::launch_reduce(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
-                                            p->gdt, p->n, t, dpk::PieceSpan{p0, p1}, accs, grads, gb->ref(),
+        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{p0, p1}, accs, grads, gb->ref(),
                                             p->stats, stream),
                          "reduce launch");
         if (s != DP_OK) return s;
     }
     if (end > begin) {
+        if (p->buckets.empty()) p->bucket_src = src;
         p->buckets.emplace_back(begin, end);
         p->bucket_elems += end - begin;
         p->bucket_mode = 1;
@@ -751,6 +768,18 @@ dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hip
         p->partials_count = t.npieces;
     }
     return DP_OK;
+}
+
+dp_status dp_accumulate_reduce_range(dp_plan* p, int64_t begin, int64_t end, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_accumulate_reduce_range: null plan");
+    return reduction_bucket(p, 0, begin, end, stream, "dp_accumulate_reduce_range");
+}
+
+dp_status dp_reduce_replicas_range(dp_plan* p, dp_role src, int64_t begin, int64_t end, hipStream_t stream) {
+    if (!p) return fail(DP_ERR_INVALID_ARG, "dp_reduce_replicas_range: null plan");
+    if (src != DP_ROLE_ACC && src != DP_ROLE_GRAD)
+        return fail(DP_ERR_INVALID_ARG, "src must be DP_ROLE_ACC or DP_ROLE_GRAD");
+    return reduction_bucket(p, src, begin, end, stream, "dp_reduce_replicas_range");
 }
 
 dp_status dp_accumulate_reduce(dp_plan* p, hipStream_t stream) {

@@ -74,7 +74,8 @@ struct dp_plan {
     bool stats_current = false;   // dp_grad_stats ran on the current g_bar
     // a call issued in buckets: the element ranges done so far, until they
     // cover [0, P).  bucket_mode 1: reduction buckets
-    // (dp_accumulate_reduce_range), complete once they cover [0, P); 2:
+    // (dp_accumulate_reduce_range, dp_reduce_replicas_range), all from the
+    // same sources, complete once they cover [0, P); 2:
     // single-pass buckets (dp_reduce_adam_range), with the update
     // hyperparameters of the first one, complete at dp_reduce_adam_finish;
     // 3: buckets of one micro-step of every replica (dp_accumulate_all_range),
@@ -84,6 +85,7 @@ struct dp_plan {
     int bucket_mode = 0;
     dp_adam_hparams bucket_hp{};
     int32_t bucket_first = 0;
+    int bucket_src = 0;  // mode 1: 0 the last micro-step fused, else the role reduced
 };
 
 namespace dpapi {

@@ -278,6 +278,21 @@ dp_status dp_accumulate_reduce(dp_plan* plan, hipStream_t stream);
  * launch, for example with events when the buckets run on other streams. */
 dp_status dp_accumulate_reduce_range(dp_plan* plan, int64_t begin, int64_t end, hipStream_t stream);
 
+/* dp_reduce_replicas over one bucket [begin, end): GBAR = (sum_r src[r]) / n
+ * in the fixed order, from the accumulators after all micro-steps (src =
+ * DP_ROLE_ACC) or from n incoming partials (src = DP_ROLE_GRAD), plus the
+ * bucket's per-chunk statistics.  The bucketed reduction of the same
+ * paragraphs as dp_accumulate_reduce_range, for callers that accumulate the
+ * last micro-step separately or receive partials in pieces.  The bucket
+ * rules, the completion once the buckets cover [0, P) and the DP_ERR_STATE
+ * of the other calls until then are those of dp_accumulate_reduce_range; the
+ * complete reduction gives, bit for bit, the g_bar and statistics of
+ * dp_reduce_replicas(src).  Every bucket of one reduction takes the same
+ * sources, including across the two bucket calls (DP_ERR_INVALID_ARG).
+ * DP_ERR_STATE with DP_ROLE_ACC when the replicas accumulated different
+ * numbers of micro-steps, or none. */
+dp_status dp_reduce_replicas_range(dp_plan* plan, dp_role src, int64_t begin, int64_t end, hipStream_t stream);
+
 /* Replica average [first page, averaging formula and reduction-order
  * paragraph]: GBAR = (sum_r SRC[r]) / n over [0, P) with a fixed pairwise order
  * (adjacent pairs by levels, an odd last term carried, binary32 partial sums),

@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     assert sorted(dp.EXPORTS) == names
     for n in names:
         assert hasattr(dp.lib, n), n
@@ -204,7 +204,7 @@ def test_bind_and_call_errors_before_any_launch():
         assert "not inside" in dp.dp_last_error()
 
 
-def test_ranged_micro_step_errors_before_any_launch():
+def test_ranged_call_errors_before_any_launch():
     with dp.Plan((1000, 24), 2, "bf16", "bf16") as p:
         h = p.handle
         with pytest.raises(dp.DpError) as e:
@@ -220,6 +220,12 @@ def test_ranged_micro_step_errors_before_any_launch():
             with pytest.raises(dp.DpError) as e:
                 dp.dp_accumulate_all_range(h, True, b, e_, stream=0)
             assert e.value.status == dp.DP_ERR_RANGE
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_replicas_range(h, dp.DP_ROLE_MASTER, 0, 256, stream=0)
+        assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:
+            dp.dp_reduce_replicas_range(h, dp.DP_ROLE_ACC, 0, 256, stream=0)  # before dp_state_init
+        assert e.value.status == dp.DP_ERR_STATE
 
 
 def test_destroy_null_is_ok():

@@ -304,3 +304,84 @@ def test_micro_step_bucket_ordering_errors():
         assert pl.read_state(stream=s)["t"] == 1
     finally:
         run.close()
+
+
+def _reduce_replicas_bucketed_run(w, steps, buckets, src):
+    """Every micro-step accumulated whole (or, for partials, none), then the
+    replica reduction from ACC or from the partials bucket by bucket
+    (dp_reduce_replicas_range); statistics and update whole."""
+    run = GpuRun(w)
+    d, pl, st = run.d, run.d.plan, run.stream
+    try:
+        states = []
+        for step in range(1, steps + 1):
+            last = 1 if w.partials else w.a
+            for k in range(1, last + 1):
+                for r in range(w.n):
+                    synth.grad_device(w, step, r, k, run.slots[r].data_ptr(), d.scale, st)
+                    pl.bind("grad", run.slots[r], r)
+                if src == "acc":
+                    pl.accumulate_all(first=(k == 1), stream=st)
+            for lo, hi in buckets:
+                pl.reduce_replicas_range(src, lo, hi, stream=st)
+            d.finish()
+            states.append(d.read_state())
+            d.scale = states[-1]["scale"]
+        return run.window(0, w.P), states
+    finally:
+        run.close()
+
+
+@pytest.mark.parametrize("name,src", [("clip_n3_a2", "acc"), ("n1_a3", "acc"), ("partials_dynamic", "grad")])
+def test_bucketed_reduce_replicas_equals_whole_bitwise(name, src):
+    """The reduction from the accumulators after every micro-step (or from
+    incoming partials) in shuffled buckets that split tensors: the g_bar,
+    statistics and state of the fused whole-range step, and the oracle's."""
+    spec = dict(CASES[name])
+    base = workloads.by_name(spec.pop("base"))
+    steps = spec.pop("steps")
+    w = base.with_(**spec)
+    rng = np.random.default_rng(17)
+    buckets = _split_inside(driver.backward_buckets(w.numel, 32 << 10), w)
+    buckets = [buckets[i] for i in rng.permutation(len(buckets))]
+    log(f"reduce_replicas_range {name} src={src}: {len(buckets)} buckets")
+    got = _reduce_replicas_bucketed_run(w, steps, buckets, src)
+    _same(got, _whole_run(w, steps))
+    ref = oracle_run(w, steps)
+    for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
+        assert_scalars_match(g, r, where=f"{name} step {s}")
+    assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+
+
+def test_reduce_replicas_bucket_errors():
+    w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=2, scaled_tensors=())
+    run = GpuRun(w)
+    pl, s = run.d.plan, run.stream
+    try:
+        for r in range(w.n):
+            run.slots[r].zero_()
+            pl.bind("grad", run.slots[r], r)
+        with pytest.raises(dp.DpError) as e:  # no micro-step accumulated yet
+            pl.reduce_replicas_range("acc", 0, 5000, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        pl.accumulate_all(True, stream=s)
+        pl.accumulate_all(False, stream=s)
+        pl.reduce_replicas_range("acc", 5000, 8000, stream=s)
+        for call in (lambda: pl.reduce_replicas_range("grad", 0, 5000, stream=s),
+                     lambda: pl.accumulate_reduce_range(0, 5000, stream=s)):
+            with pytest.raises(dp.DpError) as e:  # other sources in the same reduction
+                call()
+            assert e.value.status == dp.DP_ERR_INVALID_ARG
+        with pytest.raises(dp.DpError) as e:  # overlap
+            pl.reduce_replicas_range("acc", 5256, 8700, stream=s)
+        assert e.value.status == dp.DP_ERR_STATE
+        with pytest.raises(dp.DpError) as e:  # the reduction is half done
+            pl.reduce_replicas("acc", stream=s)
+        assert e.value.status == dp.DP_ERR_STATE and "bucketed" in e.value.message
+        pl.reduce_replicas_range("acc", 0, 5000, stream=s)
+        pl.reduce_replicas_range("acc", 8000, 8700, stream=s)  # complete
+        pl.grad_stats(False, 0.0, stream=s)
+        pl.adam_step(w.lr, w.eps, w.weight_decay, stream=s)
+        assert pl.read_state(stream=s)["t"] == 1
+    finally:
+        run.close()
