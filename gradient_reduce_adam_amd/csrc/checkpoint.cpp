@@ -15,6 +15,7 @@
 #include <memory>
 #include <new>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "dpckpt.h"
@@ -151,6 +152,18 @@ struct Fd {
     Fd& operator=(const Fd&) = delete;
 };
 
+// Removes a writer's temporary file unless it was renamed into place.
+struct TmpFile {
+    std::string path;
+    bool renamed = false;
+    explicit TmpFile(std::string p) : path(std::move(p)) {}
+    ~TmpFile() {
+        if (!renamed) (void)::unlink(path.c_str());
+    }
+    TmpFile(const TmpFile&) = delete;
+    TmpFile& operator=(const TmpFile&) = delete;
+};
+
 dp_status io_fail(const char* what, const std::string& path) {
     return fail(DP_ERR_IO, "%s %s: %s", what, path.c_str(), std::strerror(errno));
 }
@@ -195,7 +208,8 @@ dp_status sync_dir(const std::string& dir) {
 
 // Writes `data` to dir/name through a temporary file, flushed and renamed.
 dp_status replace_file(const std::string& dir, const std::string& name, const std::string& data) {
-    const std::string tmp = join(dir, ".tmp-" + name + "." + std::to_string(::getpid()));
+    TmpFile tf(join(dir, ".tmp-" + name + "." + std::to_string(::getpid())));
+    const std::string& tmp = tf.path;
     const std::string dst = join(dir, name);
     {
         Fd f(::open(tmp.c_str(), O_CREAT | O_TRUNC | O_WRONLY, 0644));
@@ -205,6 +219,7 @@ dp_status replace_file(const std::string& dir, const std::string& name, const st
         if (::fsync(f.fd) != 0) return io_fail("fsync", tmp);
     }
     if (::rename(tmp.c_str(), dst.c_str()) != 0) return io_fail("rename to", dst);
+    tf.renamed = true;
     return sync_dir(dir);
 }
 
@@ -442,7 +457,8 @@ dp_status write_shard(const std::string& dir, int64_t gen, const dp_layout* L, i
     if (gen < 0) return fail(DP_ERR_INVALID_ARG, "generation %lld < 0", static_cast<long long>(gen));
     const ShardHeader h = make_header(gen, L, P, begin, end);
     const std::string name = shard_name(gen, begin, end);
-    const std::string tmp = join(dir, ".tmp-" + name + "." + std::to_string(::getpid()));
+    TmpFile tf(join(dir, ".tmp-" + name + "." + std::to_string(::getpid())));
+    const std::string& tmp = tf.path;
     Fd f(::open(tmp.c_str(), O_CREAT | O_TRUNC | O_WRONLY, 0644));
     if (f.fd < 0) return io_fail("create", tmp);
     std::vector<uint64_t> sums(static_cast<size_t>(kArrays * h.nblocks));
@@ -469,6 +485,7 @@ dp_status write_shard(const std::string& dir, int64_t gen, const dp_layout* L, i
     if (::ftruncate(f.fd, static_cast<off_t>(h.file_bytes)) != 0) return io_fail("truncate", tmp);
     if (::fsync(f.fd) != 0) return io_fail("fsync", tmp);
     if (::rename(tmp.c_str(), join(dir, name).c_str()) != 0) return io_fail("rename", tmp);
+    tf.renamed = true;
     return DP_OK;
 }
 
@@ -783,7 +800,17 @@ dp_status dp_checkpoint_commit(dp_plan* p, const char* dir, int64_t generation, 
 
 dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t end, int32_t restore_scalars,
                              hipStream_t stream) {
-    dp_status s = device_checks(p, dir, "dp_checkpoint_load", 0);
+    if (!p || !dir) return fail(DP_ERR_INVALID_ARG, "dp_checkpoint_load: null argument");
+    if (!p->state_ready) return fail(DP_ERR_STATE, "dp_checkpoint_load before dp_state_init");
+    dp_status s = dpapi::ensure_device(p);
+    if (s != DP_OK) return s;
+    // the range goes into the current bank, so the rest of the state stays
+    // valid whether or not the caller restores it too
+    dpk::DevState st;
+    s = read_device_state(p, stream, &st);
+    if (s != DP_OK) return s;
+    const int bank = st.bank;
+    s = device_checks(p, dir, "dp_checkpoint_load", bank);
     if (s != DP_OK) return s;
     const dp_layout L = plan_layout(p);
     dp_step_state saved;
@@ -802,17 +829,14 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
              (cfg.growth_interval != c.growth_interval || cfg.backoff != c.backoff || cfg.growth != c.growth)))
             return fail(DP_ERR_STATE, "the checkpoint was taken with other optimizer settings (betas or loss scaler)");
     }
-    dpk::DevState st;
-    s = read_device_state(p, stream, &st);
-    if (s != DP_OK) return s;
     Pinned stage;
     s = alloc_pinned(&stage, read_staging_bytes(begin, end));
     if (s != DP_OK) return s;
     std::fill(want, want + kArrays, true);
     s = read_range(dir, &L, begin, end, stage.p,
                    [&](int a, int64_t lo, int64_t hi, const void* src) {
-                       return copy_role(p, *state_binding(p, a, 0), esize(a, p->pdt), lo, hi, const_cast<void*>(src),
-                                        false, stream);
+                       return copy_role(p, *state_binding(p, a, bank), esize(a, p->pdt), lo, hi,
+                                        const_cast<void*>(src), false, stream);
                    },
                    want, &saved, &cfg, &gen1);
     if (s != DP_OK) return s;
@@ -820,7 +844,7 @@ dp_status dp_checkpoint_load(dp_plan* p, const char* dir, int64_t begin, int64_t
         return fail(DP_ERR_STATE, "generation %lld was committed in %s during the load (it began at generation %lld)",
                     static_cast<long long>(gen1), dir, static_cast<long long>(gen0));
     if (restore_scalars) std::memcpy(&st, &saved, sizeof(st));
-    st.bank = 0;
+    st.bank = bank;
     hipError_t e = hipMemcpy(p->state, &st, sizeof(st), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "writing the device state");
     std::fill(p->micro.begin(), p->micro.end(), 0);

@@ -98,9 +98,10 @@ dp_status dp_checkpoint_save(dp_plan* plan, const char* dir, int64_t generation,
  * optimizer settings, as dp_ckpt_commit (synchronises stream). */
 dp_status dp_checkpoint_commit(dp_plan* plan, const char* dir, int64_t generation, hipStream_t stream);
 
-/* Restores [begin, end) of the committed checkpoint into bank 0 of MASTER,
- * EXP_AVG, EXP_AVG_SQ and into PARAM, and makes bank 0 current.  Restore
- * every range of the plan before its next step.  restore_scalars != 0 also
+/* Restores [begin, end) of the committed checkpoint into the current bank of
+ * MASTER, EXP_AVG, EXP_AVG_SQ and into PARAM; the current bank stays current,
+ * and the plan's state outside [begin, end) is left as it was.  A plan that
+ * resumes a run restores every range it updates.  restore_scalars != 0 also
  * sets the device scalar state: t, iter, the beta powers, the scale and the
  * growth tracker.  The plan's optimizer settings (dp_state_init) must then
  * equal the checkpoint's, else DP_ERR_STATE.  Accumulation restarts: the next

@@ -203,3 +203,30 @@ def test_offloaded_state_round_trip(tmp_path):
         _same(_snapshot(run), whole, "offloaded save, HBM restore")
     finally:
         run.close()
+
+
+def test_partial_restore_goes_into_the_current_bank(tmp_path):
+    """A single-pass run whose current bank is 1 restores only the first half
+    of its range from a checkpoint taken a step earlier (when bank 0 was
+    current): that half equals the checkpoint, the other half keeps the
+    current bank's values, and bank 1 stays current."""
+    w = workloads.tiny().with_(numel=RAGGED, n=2, a=1, steps=3)
+    P, h = w.P, 131072 + 3000  # a cut inside a tensor
+    run = GpuRun(w, single_pass=True)
+    try:
+        run.run(2)
+        run.d.save_checkpoint(str(tmp_path), 2, ranges=_ranges(P, 3))
+        saved, saved_st = _snapshot(run)
+        assert saved_st["bank"] == 0
+        run.step()
+        before, before_st = _snapshot(run)
+        assert before_st["bank"] == 1
+        run.d.plan.checkpoint_load(str(tmp_path), 0, h, restore_scalars=False, stream=run.stream)
+        after, after_st = _snapshot(run)
+        assert after_st["bank"] == 1 and after_st["t"] == before_st["t"]
+        for k in ("w", "m", "v", "p"):
+            assert np.array_equal(after[k][:h].view(np.uint8), saved[k][:h].view(np.uint8)), k
+            assert np.array_equal(after[k][h:].view(np.uint8), before[k][h:].view(np.uint8)), k
+            assert not np.array_equal(saved[k][h:].view(np.uint8), before[k][h:].view(np.uint8)), k
+    finally:
+        run.close()
