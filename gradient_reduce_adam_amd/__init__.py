@@ -249,8 +249,15 @@ def dp_plan_bind_flat(plan: int, role: int, replica: int, base) -> None:
     _check(lib.dp_plan_bind_flat(ctypes.c_void_p(plan), role, replica, ctypes.c_void_p(_addr(base))))
 
 
-def dp_plan_bind_tensors(plan: int, role: int, replica: int, ptrs: Iterable) -> None:
+def dp_plan_bind_tensors(plan: int, role: int, replica: int, ptrs: Iterable,
+                         num_tensors: Optional[int] = None) -> None:
+    """The library reads exactly one pointer per tensor of the plan, so the
+    list's length is checked first (num_tensors: the plan's, if known)."""
     ptrs = [_addr(p) for p in ptrs]
+    if num_tensors is None:
+        num_tensors = dp_plan_info_get(plan)["num_tensors"]
+    if len(ptrs) != num_tensors:
+        raise ValueError(f"bind_tensors: {len(ptrs)} pointers for a plan of {num_tensors} tensors")
     arr = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
     _check(lib.dp_plan_bind_tensors(ctypes.c_void_p(plan), role, replica, arr))
 
@@ -455,7 +462,7 @@ class Plan:
         dp_plan_bind_flat(self.handle, ROLES[role], replica, buf)
 
     def bind_tensors(self, role: str, bufs: Iterable, replica: int = 0) -> None:
-        dp_plan_bind_tensors(self.handle, ROLES[role], replica, bufs)
+        dp_plan_bind_tensors(self.handle, ROLES[role], replica, bufs, len(self.numel))
 
     def prepare_range(self, begin: int, end: int) -> None:
         dp_plan_prepare_range(self.handle, begin, end)

@@ -228,6 +228,15 @@ def test_ranged_call_errors_before_any_launch():
         assert e.value.status == dp.DP_ERR_STATE
 
 
+def test_bind_tensors_checks_the_pointer_count():
+    with dp.Plan((1000, 24, 7), 1, "bf16", "bf16") as p:
+        for bad in ([0x1000, 0x2000], [0x1000] * 4):
+            with pytest.raises(ValueError):
+                p.bind_tensors("master", bad)
+            with pytest.raises(ValueError):  # the low-level call asks the plan
+                dp.dp_plan_bind_tensors(p.handle, dp.DP_ROLE_MASTER, 0, bad)
+
+
 def test_destroy_null_is_ok():
     dp.dp_plan_destroy(0)
 
