@@ -225,11 +225,13 @@ class DPStep:
         dev = self.master if self.state_location == "hbm" else torch.empty(self.P, dtype=torch.float32,
                                                                             device=self.device)
         fill(dev.data_ptr())
-        torch.cuda.current_stream(self.device).wait_stream(self.stream)
+        cur = torch.cuda.current_stream(self.device)
+        cur.wait_stream(self.stream)
         self.param.copy_(dev.to(self.param.dtype))
         if dev is not self.master:
             self.master.copy_(dev)
             torch.cuda.synchronize(self.device)
+        self.stream.wait_stream(cur)  # the step's launches come after these copies
 
     # -- one step ---------------------------------------------------------
     def issue_gradients(self, produce: GradProducer, step: int) -> None:
