@@ -11,8 +11,11 @@
  * and the outputs go to state.bin (binary32 master, m, v [P] each, then the
  * 16-bit params [P]) and scalars.txt (t iter growth_tracker found_inf, then
  * beta1^t, beta2^t, scale, norm, clip as C99 hex floats).  argv[1] is the directory of
- * these files.  Exit status 0 on success; a failing call prints its status
- * and dp_last_error(). */
+ * these files.  With argv[2] = "buckets", every micro-step and the reduction
+ * run in two buckets split at the last tensor start at or before the cut, the
+ * later bucket first (dp_accumulate_all_range, dp_accumulate_reduce_range).
+ * Exit status 0 on success; a failing call prints its status and
+ * dp_last_error(). */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -79,6 +82,10 @@ int main(int argc, char** argv) {
     }
     if (fscanf(cf, "%lld", &cut) != 1 || sum != P || cut < 0 || cut > P) return 2;
     fclose(cf);
+    const int buckets = argc > 2 && strcmp(argv[2], "buckets") == 0;
+    long long bcut = 0;  /* the last tensor start at or before the cut */
+    for (long long i = 0, at = 0; i < T; at += numel[i], ++i)
+        if (at <= cut) bcut = at;
 
     const size_t np = (size_t)P;
     float* master = (float*)malloc(np * 4 + 4);
@@ -140,10 +147,17 @@ int main(int argc, char** argv) {
         for (long long k = 0; k < a; ++k) {
             for (long long r = 0; r < n; ++r)
                 CALL(dp_plan_bind_flat(plan, DP_ROLE_GRAD, (int32_t)r, g_d + ((st * a + k) * n + r) * P));
-            if (k + 1 < a)
+            if (buckets && k + 1 < a) {
+                CALL(dp_accumulate_all_range(plan, k == 0, bcut, P, s));
+                CALL(dp_accumulate_all_range(plan, k == 0, 0, bcut, s));
+            } else if (buckets) {
+                CALL(dp_accumulate_reduce_range(plan, bcut, P, s));
+                CALL(dp_accumulate_reduce_range(plan, 0, bcut, s));
+            } else if (k + 1 < a) {
                 CALL(dp_accumulate_all(plan, k == 0, s));
-            else
+            } else {
                 CALL(dp_accumulate_reduce(plan, s));
+            }
         }
         CALL(dp_grad_stats(plan, 0, max_norm, s));
         CALL(dp_adam_step(plan, &hp, cut, P, s));  /* the shards in either order */

@@ -1,8 +1,10 @@
 """The C ABI from C on the GPU: tests/c/step_gpu.c, a C99 program linked
 against libdpstep.so and the HIP runtime only (no torch, its own buffers and
 stream), runs two whole steps of a ragged workload with clipping, the update
-split into two shard calls.  Its state and scalars must match the oracle's
-run on the same seeded inputs, under the stated tolerances."""
+split into two shard calls, and again with every micro-step and the
+reduction in two buckets.  Its state and scalars must match the oracle's run
+on the same seeded inputs, under the stated tolerances, and the two runs
+must agree bit for bit."""
 import os
 import shutil
 import subprocess
@@ -38,12 +40,18 @@ def _build(tmp_path):
 
 
 def test_c_program_runs_whole_steps_through_the_abi(tmp_path):
+    results = {mode: _run_c_program(tmp_path, mode) for mode in ("whole", "buckets")}
+    for k in ("w", "m", "v", "p"):
+        assert np.array_equal(results["whole"][k].view(np.uint8), results["buckets"][k].view(np.uint8)), k
+
+
+def _run_c_program(tmp_path, mode):
     w = workloads.gpt2_small().with_(numel=RAGGED, n=3, a=2, max_norm=0.05, scaled_tensors=(4,), param_dtype="f16",
                                      steps=2)
     P, steps = w.P, w.steps
     cut = int(w.offsets[4]) + 1000  # inside tensor 4
     exe = _build(tmp_path)
-    d = tmp_path / "io"
+    d = tmp_path / f"io_{mode}"
     d.mkdir()
     dtypes = {"f16": dp.DP_F16, "bf16": dp.DP_BF16}
     with open(d / "config.txt", "w") as f:
@@ -57,8 +65,9 @@ def test_c_program_runs_whole_steps_through_the_abi(tmp_path):
             for r in range(w.n):
                 grads[s, k, r] = synth.grad_host(w, s + 1, r, k + 1, 0, P, 1.0)
     grads.tofile(d / "grads.bin")
-    log(f"C client: P={P} n={w.n} a={w.a} steps={steps} shards [0, {cut}) [{cut}, {P})")
-    r = subprocess.run([str(exe), str(d)], capture_output=True, text=True, timeout=120)
+    log(f"C client ({mode}): P={P} n={w.n} a={w.a} steps={steps} shards [0, {cut}) [{cut}, {P})")
+    r = subprocess.run([str(exe), str(d)] + (["buckets"] if mode == "buckets" else []), capture_output=True,
+                       text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
 
     raw = np.fromfile(d / "state.bin", dtype=np.uint8)
@@ -74,5 +83,6 @@ def test_c_program_runs_whole_steps_through_the_abi(tmp_path):
     ref = oracle_run(w, steps)
     assert scal["clip"] < 1.0 and scal["t"] == steps  # clipping was active on applied steps
     assert_scalars_match(scal, ref.scalars[-1], where="C client")
-    rep = assert_state_close(got, ref.state[(0, P)], where="C client")
-    log(f"  C client max ulp: {rep}")
+    rep = assert_state_close(got, ref.state[(0, P)], where=f"C client ({mode})")
+    log(f"  C client ({mode}) max ulp: {rep}")
+    return got
