@@ -385,3 +385,55 @@ def test_reduce_replicas_bucket_errors():
         assert pl.read_state(stream=s)["t"] == 1
     finally:
         run.close()
+
+
+def test_bucketed_micro_steps_on_misaligned_per_tensor_bindings():
+    """Three micro-steps of three replicas accumulated bucket by bucket (in a
+    shuffled order) into per-tensor accumulators shifted off 16-byte
+    alignment, from per-tensor gradients shifted likewise: the table path and
+    the per-element path of the ranged call.  The accumulators must equal,
+    bit for bit, those of the whole-space call on flat buffers."""
+    w = workloads.tiny().with_(numel=RAGGED, n=3, a=3)
+    P, T, off = w.P, w.T, [int(x) for x in w.offsets]
+    s = torch.cuda.current_stream().cuda_stream
+    grads = {}
+    for k in range(1, w.a + 1):
+        for r in range(w.n):
+            g = torch.empty(P, dtype=torch.int16, device="cuda")
+            synth.grad_device(w, 1, r, k, g.data_ptr(), 1.0, s)
+            grads[(k, r)] = g
+
+    def split(back):  # tensor t at element off[t] + t + 1 of its backing buffer
+        return [back[off[t] + t + 1:off[t + 1] + t + 1] for t in range(T)]
+
+    flat_acc = torch.zeros((w.n, P), dtype=torch.float32, device="cuda")
+    ref = dp.Plan(w.numel, w.n, w.grad_dtype, w.param_dtype)
+    test = dp.Plan(w.numel, w.n, w.grad_dtype, w.param_dtype)
+    acc_backs = [torch.full((P + T + 1,), float("nan"), dtype=torch.float32, device="cuda") for _ in range(w.n)]
+    try:
+        for r in range(w.n):
+            ref.bind("acc", flat_acc[r], r)
+            test.bind_tensors("acc", split(acc_backs[r]), r)
+        buckets = _split_inside(driver.backward_buckets(w.numel, 16 << 10), w)
+        rng = np.random.default_rng(19)
+        keep = []
+        for k in range(1, w.a + 1):
+            for r in range(w.n):
+                ref.bind("grad", grads[(k, r)], r)
+                gb = torch.zeros(P + T + 1, dtype=torch.int16, device="cuda")
+                for t, piece in enumerate(split(gb)):
+                    piece.copy_(grads[(k, r)][off[t]:off[t + 1]])
+                keep.append(gb)
+                test.bind_tensors("grad", split(gb), r)
+            ref.accumulate_all(first=(k == 1), stream=s)
+            for i in rng.permutation(len(buckets)):
+                lo, hi = buckets[i]
+                test.accumulate_all_range(k == 1, lo, hi, stream=s)
+            torch.cuda.synchronize()  # the per-tensor GRAD tables are rewritten for the next micro-step
+        for r in range(w.n):
+            got = torch.cat(split(acc_backs[r])).view(torch.int32).cpu().numpy()
+            want = flat_acc[r].view(torch.int32).cpu().numpy()
+            assert np.array_equal(got, want), r
+    finally:
+        ref.close()
+        test.close()
