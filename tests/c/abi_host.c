@@ -74,6 +74,11 @@ int main(int argc, char** argv) {
     dp_adam_hparams hp = {1e-3, 1e-8, 0.01};
     CHECK(dp_adam_step(plan, &hp, 0, 21003, NULL) == DP_ERR_STATE);
     CHECK(dp_adam_step(plan, &hp, 0, 21004, NULL) == DP_ERR_RANGE);
+    /* the bucket calls fail validation before any GPU work */
+    CHECK(dp_accumulate_all_range(plan, 1, 0, 256, NULL) == DP_ERR_UNBOUND);
+    CHECK(dp_accumulate_all_range(NULL, 1, 0, 256, NULL) == DP_ERR_INVALID_ARG);
+    CHECK(dp_reduce_replicas_range(plan, DP_ROLE_MASTER, 0, 256, NULL) == DP_ERR_INVALID_ARG);
+    CHECK(dp_reduce_replicas_range(plan, DP_ROLE_ACC, 0, 256, NULL) == DP_ERR_STATE); /* before dp_state_init */
     CHECK(dp_plan_drop_ranges(plan) == DP_OK); /* nothing cached: no GPU work */
     CHECK(dp_plan_drop_ranges(NULL) == DP_ERR_INVALID_ARG);
     CHECK(dp_plan_destroy(plan) == DP_OK);
