@@ -76,3 +76,53 @@ def test_full_size_sampled_parity(name, steps, single):
         if not single:
             assert np.array_equal(got[win]["gbar"].view(np.uint32), ref.gbar[steps][win].view(np.uint32)), win
     log(f"  max ulp over windows: {worst}")
+
+
+def _device_state(run):
+    """master, m, v (of the current bank) and p, as device copies."""
+    torch.cuda.synchronize()
+    w_, m_, v_ = run.d.state_tensors()
+    return [w_.clone(), m_.clone(), v_.clone(), run.d.param.clone()]
+
+
+@pytest.mark.parametrize("name,steps,single", [("gpt2_small", 2, False), ("zero3_rank_7b", 3, True)])
+def test_full_size_buckets_equal_whole(name, steps, single):
+    """The bucketed step at full size, as ``bench.py --overlap`` issues it:
+    every micro-step's accumulation and the reduction (or the single pass) in
+    buckets on a second stream, the producer writing each bucket on the
+    step's stream.  State and scalars equal the whole step's bit for bit
+    (the ZeRO-3 share's third step is skipped by its injected inf)."""
+    from gradient_reduce_adam_amd import driver
+    import synth
+    w = workloads.by_name(name)
+    run = GpuRun(w, single_pass=single)
+    try:
+        whole_states = run.run(steps)
+        whole = _device_state(run)
+    finally:
+        run.close()
+    buckets = driver.backward_buckets(w.numel, 64 << 20, split=w.partials)
+    log(f"full-size buckets {name}: {len(buckets)} buckets of 64 MB, {steps} steps, single_pass={single}")
+    run = GpuRun(w, single_pass=single)
+    slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
+    addrs = [t.data_ptr() for t in slots]
+    d = run.d
+
+    def produce(step, k, lo, hi, stream):
+        for r in range(w.n):
+            synth.grad_device(w, step, r, k, addrs[r] + 2 * lo, d.scale, stream, lo, hi)
+
+    try:
+        rs = torch.cuda.Stream()
+        states = [d.step_overlapped(addrs, produce, buckets, reduce_stream=rs, micro_buckets=True)
+                  for _ in range(steps)]
+        got = _device_state(run)
+    finally:
+        run.close()
+        del slots
+    for s, (a, b) in enumerate(zip(states, whole_states), start=1):
+        assert np.array_equal(np.array(list(a.values()), np.float64).view(np.uint64),
+                              np.array(list(b.values()), np.float64).view(np.uint64)), f"step {s} scalars"
+    for k, (x, y) in enumerate(zip(got, whole)):
+        assert torch.equal(x.view(torch.int16 if x.element_size() == 2 else torch.int32),
+                           y.view(torch.int16 if y.element_size() == 2 else torch.int32)), ("w", "m", "v", "p")[k]
