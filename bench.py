@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -350,11 +351,17 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     for _ in range(warmup):
         one_step(False)
     torch.cuda.synchronize()
+    step_marks = []  # each timed step between two events on the library's stream
     t0 = time.perf_counter()
     for _ in range(steps):
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(st_obj)
         one_step(True)
+        m1.record(st_obj)
+        step_marks.append((m0, m1))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(a.elapsed_time(b) for a, b in step_marks)
     skipped_ms = None
     if w.injections and not graph:
         # one step whose g_bar holds an inf, as the workload injects one: the
@@ -412,6 +419,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     del bufs
     torch.cuda.empty_cache()
     per_kind["skipped_step_ms"] = skipped_ms
+    per_kind["step_ms"] = None if graph else step_ms  # the eager steps; a graph replays them as one
     return elapsed, per_kind, state, ckpt, used_layout
 
 
@@ -617,6 +625,7 @@ def main():
     hbm_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     skipped_ms = per_kind.pop("skipped_step_ms", None)
+    step_ms = per_kind.pop("step_ms", None)
     # dominant kernel: the call kind that moves the most algorithmic bytes per step
     dom = max(per_param, key=lambda k: per_param[k])
     dom_bytes = launch_bytes(w, dom, single)
@@ -661,6 +670,9 @@ def main():
         "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
         "skipped_step_ms": skipped_ms,
+        # per-step event times of the timed steps: the median and the fastest
+        "step_ms_median": statistics.median(step_ms) if step_ms else None,
+        "step_ms_min": step_ms[0] if step_ms else None,
         "device": device_info(),
         "cpu_baseline": None,
     }
