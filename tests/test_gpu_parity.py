@@ -166,6 +166,15 @@ VARIANTS = {
     # the largest chunk size: every tensor here is one chunk of up to 2^18 pieces
     "max_chunk": dict(base="gpt2_small", numel=RAGGED, n=2, a=3, max_norm=0.05, scaled_tensors=(1,),
                       chunk=1 << 26, steps=3),
+    # degenerate hyperparameters: lr = 0 and no decay leave w unchanged while
+    # m and v move; betas of 0 make m = g and v = g^2 with no bias correction;
+    # eps = 1 dominates the denominator
+    "lr0_wd0": dict(base="tiny", numel=RAGGED, n=2, a=2, lr=0.0, weight_decay=0.0, steps=3),
+    "betas0_eps1": dict(base="tiny", numel=RAGGED, n=3, a=1, beta1=0.0, beta2=0.0, eps=1.0, steps=3),
+    # all-zero gradients (signed zeros from the generator) under clipping and a
+    # growing dynamic scale: norm 0, clip factor 1, the update only decays w
+    "zero_grads": dict(base="gpt2_small", numel=RAGGED, n=2, a=2, grad_sigma=0.0, max_norm=1.0, scaled_tensors=(),
+                       scaler="dynamic", init_scale=4.0, growth_interval=2, steps=4),
 }
 
 
@@ -220,6 +229,8 @@ SINGLE_PASS = {
     # sixteen single-micro-step replicas
     "n16": dict(VARIANTS["n16"]),
     "bf16_grad_f16_param": dict(VARIANTS["bf16_grad_f16_param"]),
+    "lr0_wd0": dict(VARIANTS["lr0_wd0"]),
+    "betas0_eps1": dict(VARIANTS["betas0_eps1"]),
 }
 
 
