@@ -125,8 +125,16 @@ def assert_state_close(got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], w
     for key in ("w", "m", "v"):
         g, r = got[key], ref[key]
         assert g.shape == r.shape, (key, g.shape, r.shape)
-        err = np.abs(g.astype(np.float64) - r.astype(np.float64))
-        lim = RTOL_STATE * np.abs(r.astype(np.float64)) + ATOL_STATE
+        gf, rf = g.astype(np.float64), r.astype(np.float64)
+        # a non-finite value matches only its own kind: NaN for NaN, an
+        # infinity for the infinity of the same sign
+        fin = np.isfinite(gf) & np.isfinite(rf)
+        same_kind = (np.isnan(gf) & np.isnan(rf)) | (gf == rf)
+        odd = np.flatnonzero(~fin & ~same_kind)
+        assert odd.size == 0, f"{where} {key}: {odd.size} non-finite mismatches, first at {odd[:5]}: " \
+                              f"gpu {g[odd[:5]]} oracle {r[odd[:5]]}"
+        err = np.where(fin, np.abs(np.where(fin, gf, 0.0) - np.where(fin, rf, 0.0)), 0.0)
+        lim = RTOL_STATE * np.abs(np.where(fin, rf, 0.0)) + ATOL_STATE
         bad = np.flatnonzero(err > lim)
         report[key + "_max_ulp"] = int(ulps32(g, r).max()) if g.size else 0
         assert bad.size == 0, f"{where} {key}: {bad.size} elements out of tolerance, first at {bad[:5]}: " \

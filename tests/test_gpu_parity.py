@@ -175,6 +175,12 @@ VARIANTS = {
     # growing dynamic scale: norm 0, clip factor 1, the update only decays w
     "zero_grads": dict(base="gpt2_small", numel=RAGGED, n=2, a=2, grad_sigma=0.0, max_norm=1.0, scaled_tensors=(),
                        scaler="dynamic", init_scale=4.0, growth_interval=2, steps=4),
+    # finite bf16 gradients whose binary32 sums overflow: step 1 is skipped on
+    # an inf the accumulation created; at half the scale the next steps apply,
+    # and the second moment rounds to inf in binary32
+    "overflow_in_accumulation": dict(base="gpt2_small", numel=RAGGED, n=2, a=4, grad_sigma=5e37, max_norm=0.0,
+                                     scaled_tensors=(), scaler="dynamic", init_scale=1.0, growth_interval=2,
+                                     steps=3),
 }
 
 
@@ -231,6 +237,7 @@ SINGLE_PASS = {
     "bf16_grad_f16_param": dict(VARIANTS["bf16_grad_f16_param"]),
     "lr0_wd0": dict(VARIANTS["lr0_wd0"]),
     "betas0_eps1": dict(VARIANTS["betas0_eps1"]),
+    "overflow_in_accumulation": dict(VARIANTS["overflow_in_accumulation"]),
 }
 
 
