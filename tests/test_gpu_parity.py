@@ -495,6 +495,15 @@ def test_empty_plan_and_empty_tensors():
         p.adam_step(1e-3, 1e-8, 0.0, stream=s)
         st = p.read_state(stream=s)
         assert st["t"] == 1 and st["found_inf"] == 0 and st["norm"] == 0.0
+        # the bucket calls: one empty bucket covers [0, 0), so each completes at once
+        p.accumulate_all_range(True, 0, 0, stream=s)
+        p.accumulate_all_range(False, 0, 0, stream=s)
+        p.reduce_replicas_range("acc", 0, 0, stream=s)
+        p.grad_stats(scan=False, max_norm=1.0, stream=s)
+        p.adam_step(1e-3, 1e-8, 0.0, stream=s)
+        p.accumulate_reduce_range(0, 0, stream=s)
+        p.grad_stats(scan=False, max_norm=1.0, stream=s)
+        assert p.read_state(stream=s)["t"] == 3
     w = workloads.tiny().with_(numel=(0, 5000, 0, 0, 3, 0), n=2, a=2, steps=2)
     _full_parity(w, 2, label="zero-size tensors")
 
@@ -512,6 +521,10 @@ def test_single_pass_empty_plan():
         p.reduce_adam_step(1e-3, 1e-8, 0.0, stream=s)
         st = p.read_state(stream=s)
         assert st["t"] == 1 and st["found_inf"] == 0 and st["norm"] == 0.0 and st["bank"] == 1
+        p.reduce_adam_range(1e-3, 1e-8, 0.0, 0, 0, stream=s)  # one empty bucket covers [0, 0)
+        p.reduce_adam_finish(stream=s)
+        st = p.read_state(stream=s)
+        assert st["t"] == 2 and st["bank"] == 0
 
 
 def test_empty_shard_is_a_noop():
