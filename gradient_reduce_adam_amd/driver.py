@@ -17,7 +17,11 @@ the last micro-step, the replica average, the statistics and the update are
 one ``dp_reduce_adam_step`` over two state banks; again the same bits.
 Gradients come from a caller-supplied producer, standing in for the backward
 pass; the fused sequence needs the n replicas' gradients of one micro-step at
-once.
+once.  ``step_overlapped`` issues the same step bucket by bucket
+(``dp_accumulate_reduce_range``, or ``dp_reduce_adam_range`` and
+``dp_reduce_adam_finish`` for the single pass, and with ``micro_buckets`` also
+``dp_accumulate_all_range`` for the earlier micro-steps), on a second stream
+as the producer writes each bucket; again the same bits.
 
 HBM layout (flat parameter space of P elements, tensors in list order; see
 ``layout`` for where the arrays sit relative to each other):
