@@ -252,6 +252,30 @@ def measure_pcie_copies(nbytes: int = 1 << 30, reps: int = 5) -> dict:
     return {"h2d_gbps": run(True, False), "d2h_gbps": run(False, True), "both_gbps": run(True, True)}
 
 
+def measure_runtime_copy(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """The HIP runtime's own device-to-device copy of 1 GiB (torch ``copy_``),
+    timed with HIP events: a per-machine reference point measured in the same
+    process, since machines differ by a few percent.  It is not a ceiling: on
+    MI355X it reaches about 5 TB/s, below the library's streaming kernels."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": 2 * nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
+            "what": "HIP runtime device-to-device copy (torch copy_), read + write bytes per second"}
+
+
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
             ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct",
             layout: str = "auto", log_path: str = ""):
@@ -674,6 +698,7 @@ def main():
         "step_ms_median": statistics.median(step_ms) if step_ms else None,
         "step_ms_min": step_ms[0] if step_ms else None,
         "device": device_info(),
+        "runtime_copy": measure_runtime_copy(),
         "cpu_baseline": None,
     }
     if args.state == "host":
