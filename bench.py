@@ -252,28 +252,39 @@ def measure_pcie_copies(nbytes: int = 1 << 30, reps: int = 5) -> dict:
     return {"h2d_gbps": run(True, False), "d2h_gbps": run(False, True), "both_gbps": run(True, True)}
 
 
-def measure_runtime_copy(nbytes: int = 1 << 30, reps: int = 10) -> dict:
-    """The HIP runtime's own device-to-device copy of 1 GiB (torch ``copy_``),
-    timed with HIP events: a per-machine reference point measured in the same
-    process, since machines differ by a few percent.  It is not a ceiling: on
-    MI355X it reaches about 5 TB/s, below the library's streaming kernels."""
+def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """Bandwidth references measured live on this GPU, in the same process
+    (machines differ by a few percent): a copy and a read by one-shot wave64
+    kernels shaped like the library's (16 bytes per lane, nontemporal), and
+    the HIP runtime's own device-to-device copy (torch ``copy_``), which is
+    slower and no ceiling."""
     import torch
 
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    import synth
+
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    s = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn) -> float:
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_copy = timed(lambda: synth.stream_probe("copy", src.data_ptr(), dst.data_ptr(), nbytes, s))
+    t_read = timed(lambda: synth.stream_probe("read", src.data_ptr(), 0, nbytes, s))
+    t_rt = timed(lambda: dst.copy_(src))
     del src, dst
     torch.cuda.empty_cache()
-    return {"gbps": 2 * nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
-            "what": "HIP runtime device-to-device copy (torch copy_), read + write bytes per second"}
+    return {"copy_gbps": 2 * nbytes / t_copy / 1e9, "read_gbps": nbytes / t_read / 1e9,
+            "runtime_copy_gbps": 2 * nbytes / t_rt / 1e9, "bytes": nbytes,
+            "what": "one-shot wave64 copy and read (16 B per lane, nontemporal); runtime copy = torch copy_"}
 
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
@@ -698,7 +709,7 @@ def main():
         "step_ms_median": statistics.median(step_ms) if step_ms else None,
         "step_ms_min": step_ms[0] if step_ms else None,
         "device": device_info(),
-        "runtime_copy": measure_runtime_copy(),
+        "measured_ceilings": measure_ceilings(),
         "cpu_baseline": None,
     }
     if args.state == "host":

@@ -132,6 +132,9 @@ def _gpu_lib():
                                                   ctypes.c_int, ctypes.c_void_p]
         lib.synth_busy_device.restype = ctypes.c_int
         lib.synth_busy_device.argtypes = [ctypes.c_double, ctypes.c_void_p]
+        lib.synth_stream_probe.restype = ctypes.c_int
+        lib.synth_stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p]
         _gpu = lib
     return _gpu
 
@@ -229,6 +232,15 @@ def grad_device(w, step: int, replica: int, micro: int, out_ptr: int, loss_scale
 def master_device(w, out_ptr: int, stream: int, lo: int = 0, hi: Optional[int] = None) -> None:
     hi = w.P if hi is None else hi
     device_normal(master_key(w), lo, hi - lo, scale_constant(w.master_sigma), "f32", out_ptr, stream)
+
+
+def stream_probe(kind: str, src_ptr: int, dst_ptr: int, nbytes: int, stream: int) -> None:
+    """One pass of a bandwidth reference kernel (benchmark infrastructure):
+    kind "copy" copies nbytes from src to dst, "read" reads nbytes of src."""
+    rc = _gpu_lib().synth_stream_probe({"copy": 0, "read": 1}[kind], ctypes.c_void_p(src_ptr),
+                                       ctypes.c_void_p(dst_ptr), int(nbytes), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_probe failed with code {rc}")
 
 
 def busy_device(flops: float, stream: int) -> None:

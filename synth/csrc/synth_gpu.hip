@@ -123,9 +123,56 @@ __global__ void __launch_bounds__(kBusyThreads) busy_mfma(int64_t iters, float* 
     if (s == -1.0f && sink != nullptr) sink[0] = s;
 }
 
+// Bandwidth references for the benchmark, shaped like the library's streaming
+// kernels: one-shot wave64 workgroups, 16-byte accesses per lane, nontemporal
+// hints.  The copy reads and writes one KiB per wave; the read takes four KiB
+// per wave (a single KiB leaves it bound by how fast waves launch), sums them
+// and stores only when the sum equals a value the caller's data never holds.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define SYNTH_GLOBAL __attribute__((address_space(1)))
+
+__global__ void __launch_bounds__(64) stream_copy(const f32x4* src, f32x4* dst, int64_t nvec) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
+    if (i < nvec)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(((const SYNTH_GLOBAL f32x4*)src) + i),
+                                    ((SYNTH_GLOBAL f32x4*)dst) + i);
+}
+
+__global__ void __launch_bounds__(64) stream_read(const f32x4* src, int64_t nvec, float* sink) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t i = base + 64 * j;
+        if (i < nvec) {
+            const f32x4 v = __builtin_nontemporal_load(((const SYNTH_GLOBAL f32x4*)src) + i);
+            s += (v.x + v.y) + (v.z + v.w);
+        }
+    }
+    if (s == -1.0f && sink != nullptr) sink[0] = s;
+}
+
 }  // namespace
 
 extern "C" {
+
+// One pass of a bandwidth reference over `bytes` bytes (a multiple of 1024):
+// kind 0 copies src to dst, kind 1 reads src (dst unused).  Returns 0, -1 on a
+// bad argument, or the HIP error code.
+int synth_stream_probe(int kind, const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    if (src == nullptr || bytes <= 0 || bytes % 1024 != 0 || (kind == 0 && dst == nullptr) || kind < 0 || kind > 1)
+        return -1;
+    const int64_t nvec = bytes / 16;
+    const int64_t blocks = kind == 0 ? nvec / 64 : (nvec + 255) / 256;
+    if (blocks > (int64_t{1} << 31) - 1) return -1;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (kind == 0)
+        hipLaunchKernelGGL(stream_copy, grid, dim3(64), 0, stream, static_cast<const f32x4*>(src),
+                           static_cast<f32x4*>(dst), nvec);
+    else
+        hipLaunchKernelGGL(stream_read, grid, dim3(64), 0, stream, static_cast<const f32x4*>(src), nvec, nullptr);
+    return static_cast<int>(hipGetLastError());
+}
 
 // Overwrites one 16-bit element (used to inject a non-finite gradient value).
 int synth_poke_u16(void* p, uint32_t bits, hipStream_t stream) {

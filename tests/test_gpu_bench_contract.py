@@ -34,7 +34,8 @@ def test_bench_prints_the_contract_line():
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert rf["traffic"] is None or rf["traffic"] > 0
-    assert d["runtime_copy"]["gbps"] > 0
+    mc = d["measured_ceilings"]
+    assert mc["copy_gbps"] > 0 and mc["read_gbps"] > 0 and mc["runtime_copy_gbps"] > 0
     # per-step event times beside the wall-clock mean
     assert 0 < d["step_ms_min"] <= d["step_ms_median"]
     cb = d["cpu_baseline"]
