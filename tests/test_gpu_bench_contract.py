@@ -13,9 +13,10 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def test_bench_prints_the_contract_line():
+def test_bench_prints_the_contract_line(tmp_path):
+    log_path = tmp_path / "steps.jsonl"
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", "tiny", "--steps", "3",
-                        "--warmup", "1", "--cpu-sample", str(1 << 16)],
+                        "--warmup", "1", "--cpu-sample", str(1 << 16), "--log-steps", str(log_path)],
                        capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-4000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
@@ -41,3 +42,9 @@ def test_bench_prints_the_contract_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == d["unit"]
     assert isinstance(cb["sample"], str) and cb["sample"]
+    # the per-step log: one line per extra step, after everything timed
+    recs = [json.loads(ln) for ln in open(log_path)]
+    assert len(recs) == 3
+    assert [x["iter"] for x in recs] == [d["final_state"]["t"] + i for i in (1, 2, 3)]
+    for x in recs:
+        assert x["workload"] == "tiny" and x["found_inf"] == 0 and x["step_ms"] > 0 and x["call_ms"]
