@@ -38,7 +38,7 @@ KERNEL_SRC = (os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hi
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="gpt2_small",
                     help="tiny | gpt2_small | zero3_rank_7b | unsharded_7b | tp_column_slice")
