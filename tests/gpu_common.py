@@ -35,7 +35,7 @@ def log(msg: str) -> None:
 # ----------------------------------------------------------------------------
 # GPU side
 # ----------------------------------------------------------------------------
-class GpuRun:
+class DeviceRun:
     """A workload on the GPU: the library's driver plus device-generated inputs."""
 
     def __init__(self, w, shards=None, chunk_elems: int = 0, fused: bool = True, single_pass: bool = False,

@@ -17,7 +17,7 @@ import gradient_reduce_adam_amd as dp
 import synth
 from synth import workloads
 
-from gpu_common import GpuRun, log
+from gpu_common import DeviceRun, log
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,7 @@ def test_random_bucket_schedules_equal_whole(name, seed):
     steps = spec.pop("steps")
     w = base.with_(**spec)
     single = w.max_norm == 0.0
-    ref_run = GpuRun(w, single_pass=single)
+    ref_run = DeviceRun(w, single_pass=single)
     try:
         ref_states = ref_run.run(steps)
         ref = _snapshot(ref_run)
@@ -84,7 +84,7 @@ def test_random_bucket_schedules_equal_whole(name, seed):
 
     rng = np.random.default_rng(1000 + seed)
     grid = _grid(w)
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     d, pl, s = run.d, run.d.plan, run.stream
     lr, eps, wd = w.lr, w.eps, w.weight_decay
     routes = []

@@ -16,7 +16,7 @@ import synth
 from gradient_reduce_adam_amd import driver
 from synth import workloads
 
-from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def _split_inside(buckets, w):
 
 
 def _bucketed_run(w, steps, buckets, two_streams, single=False, micro=False):
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     d = run.d
     slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
     addrs = [t.data_ptr() for t in slots]
@@ -60,7 +60,7 @@ def _bucketed_run(w, steps, buckets, two_streams, single=False, micro=False):
 
 
 def _whole_run(w, steps, single=False):
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     try:
         states = run.run(steps)
         return run.window(0, w.P), states
@@ -115,7 +115,7 @@ def test_shuffled_buckets_equal_whole_bitwise():
 
 def test_bucket_ordering_errors():
     w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=1, scaled_tensors=())
-    run = GpuRun(w)
+    run = DeviceRun(w)
     d, pl, s = run.d, run.d.plan, run.stream
     try:
         for r in range(w.n):
@@ -184,7 +184,7 @@ def test_shuffled_single_pass_buckets_equal_whole_bitwise():
 
 def test_single_pass_bucket_ordering_errors():
     w = workloads.tiny().with_(numel=(5000, 3000, 700), n=2, a=1)
-    run = GpuRun(w, single_pass=True)
+    run = DeviceRun(w, single_pass=True)
     pl, s = run.d.plan, run.stream
     lr, eps, wd = w.lr, w.eps, w.weight_decay
     try:
@@ -263,7 +263,7 @@ def test_shuffled_micro_step_buckets_equal_whole_bitwise():
 
 def test_micro_step_bucket_ordering_errors():
     w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=3, scaled_tensors=())
-    run = GpuRun(w)
+    run = DeviceRun(w)
     pl, s = run.d.plan, run.stream
     try:
         for r in range(w.n):
@@ -310,7 +310,7 @@ def _reduce_replicas_bucketed_run(w, steps, buckets, src):
     """Every micro-step accumulated whole (or, for partials, none), then the
     replica reduction from ACC or from the partials bucket by bucket
     (dp_reduce_replicas_range); statistics and update whole."""
-    run = GpuRun(w)
+    run = DeviceRun(w)
     d, pl, st = run.d, run.d.plan, run.stream
     try:
         states = []
@@ -355,7 +355,7 @@ def test_bucketed_reduce_replicas_equals_whole_bitwise(name, src):
 
 def test_reduce_replicas_bucket_errors():
     w = workloads.gpt2_small().with_(numel=(5000, 3000, 700), n=2, a=2, scaled_tensors=())
-    run = GpuRun(w)
+    run = DeviceRun(w)
     pl, s = run.d.plan, run.stream
     try:
         for r in range(w.n):

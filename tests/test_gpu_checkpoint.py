@@ -11,7 +11,7 @@ import torch
 import gradient_reduce_adam_amd as dp
 from synth import workloads
 
-from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -65,14 +65,14 @@ def test_recovery_drill_resharded_bitwise(name, tmp_path):
     save_sh = None if single else _ranges(P, ks)
     load_sh = None if single else _ranges(P, kl)
     # uninterrupted
-    run = GpuRun(w, shards=save_sh, single_pass=single)
+    run = DeviceRun(w, shards=save_sh, single_pass=single)
     try:
         run.run(steps)
         whole = _snapshot(run)
     finally:
         run.close()
     # interrupted after save_at steps, saved over ks ranges
-    run = GpuRun(w, shards=save_sh, single_pass=single)
+    run = DeviceRun(w, shards=save_sh, single_pass=single)
     try:
         run.run(save_at)
         run.d.save_checkpoint(str(tmp_path), save_at, ranges=_ranges(P, ks))
@@ -80,7 +80,7 @@ def test_recovery_drill_resharded_bitwise(name, tmp_path):
     finally:
         run.close()
     # a fresh process state: new plan and buffers, restored over kl ranges
-    run = GpuRun(w, shards=load_sh, single_pass=single)
+    run = DeviceRun(w, shards=load_sh, single_pass=single)
     try:
         st = run.d.load_checkpoint(str(tmp_path), ranges=_ranges(P, kl))
         assert st["iter"] == save_at and st["bank"] == 0
@@ -102,7 +102,7 @@ def test_save_and_load_through_per_tensor_bindings(tmp_path):
     checkpoints back on the host: the same bits everywhere."""
     w = workloads.tiny().with_(numel=(1001, 4099, 65536 + 3, 7), n=2, a=1, steps=2)
     P, off, T = w.P, w.offsets, w.T
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.run(2)
         (tmp_path / "a").mkdir()
@@ -148,7 +148,7 @@ def test_save_and_load_through_per_tensor_bindings(tmp_path):
 
 def test_load_errors(tmp_path):
     w = workloads.tiny().with_(numel=(5000, 3), n=1, a=1, steps=1)
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         with pytest.raises(dp.DpError) as e:  # nothing committed yet
             run.d.plan.checkpoint_load(str(tmp_path), stream=run.stream)
@@ -158,14 +158,14 @@ def test_load_errors(tmp_path):
     finally:
         run.close()
     other = w.with_(numel=(5000, 4))
-    run = GpuRun(other)
+    run = DeviceRun(other)
     try:
         with pytest.raises(dp.DpError) as e:
             run.d.plan.checkpoint_load(str(tmp_path), stream=run.stream)
         assert e.value.status == dp.DP_ERR_BAD_LAYOUT
     finally:
         run.close()
-    run = GpuRun(w.with_(beta2=0.99))
+    run = DeviceRun(w.with_(beta2=0.99))
     try:
         before = _snapshot(run)
         with pytest.raises(dp.DpError) as e:
@@ -183,19 +183,19 @@ def test_offloaded_state_round_trip(tmp_path):
     uninterrupted run."""
     w = workloads.tiny().with_(numel=RAGGED, n=2, a=2, steps=4)
     P = w.P
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.run(4)
         whole = _snapshot(run)
     finally:
         run.close()
-    run = GpuRun(w, state_location="host")
+    run = DeviceRun(w, state_location="host")
     try:
         run.run(2)
         run.d.save_checkpoint(str(tmp_path), 2, ranges=_ranges(P, 3))
     finally:
         run.close()
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.d.load_checkpoint(str(tmp_path), ranges=_ranges(P, 2))
         run.step()
@@ -212,7 +212,7 @@ def test_partial_restore_goes_into_the_current_bank(tmp_path):
     current bank's values, and bank 1 stays current."""
     w = workloads.tiny().with_(numel=RAGGED, n=2, a=1, steps=3)
     P, h = w.P, 131072 + 3000  # a cut inside a tensor
-    run = GpuRun(w, single_pass=True)
+    run = DeviceRun(w, single_pass=True)
     try:
         run.run(2)
         run.d.save_checkpoint(str(tmp_path), 2, ranges=_ranges(P, 3))

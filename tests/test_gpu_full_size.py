@@ -17,7 +17,7 @@ import torch
 
 from synth import workloads
 
-from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run, sample_windows
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, sample_windows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -49,7 +49,7 @@ def test_full_size_sampled_parity(name, steps, single):
     log(f"full size {name}: P={w.P} T={w.T} n={w.n} a={w.a} steps={steps} single_pass={single} "
         f"windows={len(wins)} ({sum(h - l for l, h in wins)} elements)")
     t0 = time.time()
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     try:
         states = run.run(steps)
         got = {win: run.window(*win) for win in wins}
@@ -95,7 +95,7 @@ def test_full_size_buckets_equal_whole(name, steps, single):
     from gradient_reduce_adam_amd import driver
     import synth
     w = workloads.by_name(name)
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     try:
         whole_states = run.run(steps)
         whole = _device_state(run)
@@ -103,7 +103,7 @@ def test_full_size_buckets_equal_whole(name, steps, single):
         run.close()
     buckets = driver.backward_buckets(w.numel, 64 << 20, split=w.partials)
     log(f"full-size buckets {name}: {len(buckets)} buckets of 64 MB, {steps} steps, single_pass={single}")
-    run = GpuRun(w, single_pass=single)
+    run = DeviceRun(w, single_pass=single)
     slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
     addrs = [t.data_ptr() for t in slots]
     d = run.d

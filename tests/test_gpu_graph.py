@@ -8,7 +8,7 @@ import torch
 import synth
 from synth import workloads
 
-from gpu_common import GpuRun, log
+from gpu_common import DeviceRun, log
 
 pytestmark = pytest.mark.gpu
 
@@ -30,14 +30,14 @@ def test_graph_replays_equal_eager_steps(name):
     w = workloads.by_name(spec.pop("base")).with_(**spec)
     steps = 5
     log(f"graph {name}: P={w.P} n={w.n} a={w.a} single_pass={single}")
-    eager = GpuRun(w, single_pass=single)
+    eager = DeviceRun(w, single_pass=single)
     try:
         ref_states = eager.run(steps)
         ref = eager.window(0, w.P)
     finally:
         eager.close()
     last = 1 if w.partials else w.a
-    run = GpuRun(w, single_pass=single, stream=torch.cuda.Stream())
+    run = DeviceRun(w, single_pass=single, stream=torch.cuda.Stream())
     d, st = run.d, run.d.stream.cuda_stream
     bufs = [[torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)] for _ in range(last)]
     slots = [[b.data_ptr() for b in row] for row in bufs]

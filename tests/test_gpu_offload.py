@@ -6,7 +6,7 @@ import pytest
 
 from synth import workloads
 
-from gpu_common import GpuRun, assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ def test_host_state_equals_hbm_state_bitwise(name):
     log(f"offload {name}: P={w.P} steps={steps} single_pass={single}")
     outs = []
     for loc in ("hbm", "host"):
-        run = GpuRun(w, single_pass=single, state_location=loc)
+        run = DeviceRun(w, single_pass=single, state_location=loc)
         try:
             if loc == "host":
                 assert not run.d.master.is_cuda and run.d.master.is_pinned()
@@ -55,7 +55,7 @@ def test_staged_offload_equals_direct_bitwise():
     shards = [(0, 100003), (100003, w.P)]
     outs = []
     for off in ("direct", "staged"):
-        run = GpuRun(w, shards=shards, state_location="host", offload=off, stage_elems=65536)
+        run = DeviceRun(w, shards=shards, state_location="host", offload=off, stage_elems=65536)
         try:
             st = run.run(4)
             outs.append((run.window(0, w.P), st))

@@ -11,7 +11,7 @@ from synth import workloads
 from gradient_reduce_adam_amd import driver
 import gradient_reduce_adam_amd as dp
 
-from gpu_common import (GpuRun, assert_scalars_match, assert_state_close, log, oracle_run, ulps32)
+from gpu_common import (DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, ulps32)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def test_accumulators_and_gbar_bit_exact(gdt, n, a, chunk):
     log(f"accumulate/reduce {gdt} n={n} a={a} chunk={chunk} P={w.P}")
     ref_gbar = oracle_run(w, 1, keep_gbar=(1,)).gbar[1][(0, w.P)]
     # per-replica calls: every accumulator, then g_bar
-    run = GpuRun(w, chunk_elems=chunk, fused=False)
+    run = DeviceRun(w, chunk_elems=chunk, fused=False)
     try:
         run.d.issue_gradients(run.produce, 1)
         torch.cuda.synchronize()
@@ -76,7 +76,7 @@ def test_accumulators_and_gbar_bit_exact(gdt, n, a, chunk):
         run.close()
     # all replicas per launch, the last micro-step fused with the reduction:
     # the accumulators hold micro-steps 1 .. a-1, g_bar the same bits
-    run = GpuRun(w, chunk_elems=chunk, fused=True)
+    run = DeviceRun(w, chunk_elems=chunk, fused=True)
     try:
         run.d.issue_gradients(run.produce, 1)
         torch.cuda.synchronize()
@@ -96,7 +96,7 @@ def test_accumulators_and_gbar_bit_exact(gdt, n, a, chunk):
 def test_partials_reduction_bit_exact():
     w = workloads.zero3_rank_7b().with_(numel=(200003,), injections=())
     log(f"partials reduce P={w.P}")
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.d.issue_gradients(run.produce, 1)
         ref = oracle_run(w, 1, keep_gbar=(1,)).gbar[1][(0, w.P)]
@@ -113,7 +113,7 @@ def _full_parity(w, steps, shards=None, chunk=0, label="", single_pass=False):
     log(f"full parity {label or w.name}: P={w.P} T={w.T} n={w.n} a={w.a} {w.grad_dtype}/{w.param_dtype} "
         f"clip={w.max_norm} scaler={w.scaler} steps={steps} shards={0 if shards is None else len(shards)} "
         f"single_pass={single_pass}")
-    run = GpuRun(w, shards=shards, chunk_elems=chunk, single_pass=single_pass)
+    run = DeviceRun(w, shards=shards, chunk_elems=chunk, single_pass=single_pass)
     try:
         gpu_states = run.run(steps)
         got = run.window(0, w.P)
@@ -206,7 +206,7 @@ def test_per_replica_sequence_equals_fused_bitwise(name):
     log(f"per-replica vs fused {name}")
     outs = []
     for fused in (False, True):
-        run = GpuRun(w, chunk_elems=chunk, fused=fused)
+        run = DeviceRun(w, chunk_elems=chunk, fused=fused)
         try:
             st = run.run(steps)
             outs.append((run.window(0, w.P), st))
@@ -261,7 +261,7 @@ def test_single_pass_equals_two_pass_bitwise(name):
     log(f"single pass vs two passes {name}")
     outs = []
     for single in (False, True):
-        run = GpuRun(w, chunk_elems=chunk, single_pass=single)
+        run = DeviceRun(w, chunk_elems=chunk, single_pass=single)
         try:
             st = run.run(steps)
             outs.append((run.window(0, w.P), st))
@@ -283,7 +283,7 @@ def test_single_pass_skip_leaves_state_and_params_unchanged():
     """A non-finite g_bar discards the speculative update: the current bank,
     the parameters and every scalar but iter and the scale stay as they were."""
     w = workloads.zero3_rank_7b().with_(numel=(70001, 3000), n=3, injections=((2, 1, 1, 4321, float("inf")),))
-    run = GpuRun(w, single_pass=True)
+    run = DeviceRun(w, single_pass=True)
     try:
         s1 = run.step()
         before = run.window(0, w.P)
@@ -306,7 +306,7 @@ def test_spread_layout_equals_packed_bitwise(single):
     w = workloads.tiny().with_(numel=RAGGED, n=3, a=2, steps=3)
     outs = []
     for layout in ("packed", "spread"):
-        run = GpuRun(w, single_pass=single, layout=layout)
+        run = DeviceRun(w, single_pass=single, layout=layout)
         try:
             assert run.d.layout == layout
             st = run.run(3)
@@ -327,7 +327,7 @@ def test_sharded_update_equals_unsharded_bitwise():
     shards = [(0, 1), (1, 3001), (3001, 3020), (3020, 50000), (50000, 50000), (50000, 150000), (150000, P - 1),
               (P - 1, P)]
     got_sh, ref, _ = _full_parity(w, 3, shards=shards, label="sharded")
-    run = GpuRun(w)
+    run = DeviceRun(w)
     try:
         run.run(3)
         got_full = run.window(0, P)
@@ -341,7 +341,7 @@ def test_bitwise_reproducible():
     w = workloads.gpt2_small().with_(numel=RAGGED, n=8, a=2, max_norm=0.05, scaled_tensors=(3,), steps=2)
     outs = []
     for _ in range(2):
-        run = GpuRun(w)
+        run = DeviceRun(w)
         try:
             st = run.run(2)
             outs.append((run.window(0, w.P), st))
@@ -529,7 +529,7 @@ def test_single_pass_empty_plan():
 
 def test_empty_shard_is_a_noop():
     w = workloads.tiny().with_(numel=(10000,), n=1, a=1, steps=1)
-    run = GpuRun(w, shards=[(0, 0), (5000, 5000)])
+    run = DeviceRun(w, shards=[(0, 0), (5000, 5000)])
     try:
         before = run.window(0, w.P)
         run.run(1)
