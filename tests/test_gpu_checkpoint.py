@@ -230,3 +230,59 @@ def test_partial_restore_goes_into_the_current_bank(tmp_path):
             assert not np.array_equal(saved[k][h:].view(np.uint8), before[k][h:].view(np.uint8)), k
     finally:
         run.close()
+
+
+def _random_ranges(rng, P):
+    """A random partition of [0, P) into 1-8 ranges with arbitrary cuts (empty
+    ranges included)."""
+    cuts = sorted([0, P] + [int(x) for x in rng.integers(0, P + 1, int(rng.integers(0, 8)))])
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_recovery_drills_bitwise(seed, tmp_path):
+    """Seeded drills: a random ragged layout, update path (two-pass with
+    clipping or a dynamic scale, or the single pass whose current bank is
+    either), interruption point, and save and restore partitions with
+    arbitrary cuts.  The resumed run equals the uninterrupted one bit for bit."""
+    rng = np.random.default_rng(7000 + seed)
+    T = int(rng.integers(1, 12))
+    numel = tuple(int(x) for x in rng.integers(0, 30000, T))
+    if sum(numel) == 0:
+        numel = (5000,)
+    single = bool(rng.random() < 0.5)
+    base = workloads.tiny() if single else workloads.gpt2_small()
+    spec = dict(numel=numel, n=int(rng.integers(1, 5)), a=int(rng.integers(1, 4)), steps=int(rng.integers(3, 6)))
+    if not single:
+        spec.update(max_norm=float(rng.choice([0.0, 0.05])), scaled_tensors=())
+    if rng.random() < 0.5:
+        spec.update(scaler="dynamic", init_scale=256.0, growth_interval=2)
+    w = base.with_(**spec)
+    P, steps = w.P, w.steps
+    save_at = int(rng.integers(1, steps))
+    save_r, load_r = _random_ranges(rng, P), _random_ranges(rng, P)
+    log(f"drill {seed}: P={P} T={T} n={w.n} a={w.a} single={single} clip={w.max_norm} scaler={w.scaler} "
+        f"steps={steps} save after {save_at} as {len(save_r)}, restore as {len(load_r)}")
+    run = DeviceRun(w, single_pass=single)
+    try:
+        run.run(steps)
+        whole = _snapshot(run)
+    finally:
+        run.close()
+    run = DeviceRun(w, single_pass=single)
+    try:
+        run.run(save_at)
+        run.d.save_checkpoint(str(tmp_path), save_at, ranges=save_r)
+    finally:
+        run.close()
+    run = DeviceRun(w, single_pass=single)
+    try:
+        if single and save_at % 2 == 1:  # restore into a plan whose bank 1 is current
+            run.run(1)
+        st = run.d.load_checkpoint(str(tmp_path), ranges=load_r)
+        assert st["iter"] == save_at
+        for _ in range(steps - save_at):
+            run.step()
+        _same(_snapshot(run), whole, f"drill {seed}")
+    finally:
+        run.close()
