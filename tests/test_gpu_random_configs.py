@@ -48,16 +48,17 @@ def _draw(seed):
     if not single and rng.random() < 0.5:
         cuts = sorted(set([0, P] + [int(x) for x in rng.integers(0, P + 1, int(rng.integers(1, 5)))]))
         shards = list(zip(cuts[:-1], cuts[1:]))
-    return w, chunk, single, shards
+    location = "host" if rng.random() < 0.25 else "hbm"  # the state offloaded to pinned host memory
+    return w, chunk, single, shards, location
 
 
 @pytest.mark.parametrize("seed", range(32))
 def test_random_configuration_matches_oracle(seed):
-    w, chunk, single, shards = _draw(seed)
+    w, chunk, single, shards, location = _draw(seed)
     log(f"seed {seed}: P={w.P} T={w.T} n={w.n} a={w.a} {w.grad_dtype}/{w.param_dtype} clip={w.max_norm} "
         f"scaler={w.scaler} partials={w.partials} chunk={chunk or 'default'} single={single} "
-        f"shards={None if shards is None else len(shards)} injections={w.injections}")
-    run = DeviceRun(w, shards=shards, chunk_elems=chunk, single_pass=single)
+        f"shards={None if shards is None else len(shards)} injections={w.injections} state={location}")
+    run = DeviceRun(w, shards=shards, chunk_elems=chunk, single_pass=single, state_location=location)
     try:
         states = run.run(w.steps)
         got = run.window(0, w.P)
