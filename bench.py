@@ -257,12 +257,15 @@ def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
     (machines differ by a few percent): a copy and a read by one-shot wave64
     kernels shaped like the library's (16 bytes per lane, nontemporal), and
     the HIP runtime's own device-to-device copy (torch ``copy_``), which is
-    slower and no ceiling."""
+    slower and no ceiling.  The source holds random bytes: HBM moves a
+    constant fill 2-4% faster than the random values the workloads carry."""
     import torch
 
     import synth
 
-    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=gen)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
 
@@ -284,7 +287,7 @@ def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
     torch.cuda.empty_cache()
     return {"copy_gbps": 2 * nbytes / t_copy / 1e9, "read_gbps": nbytes / t_read / 1e9,
             "runtime_copy_gbps": 2 * nbytes / t_rt / 1e9, "bytes": nbytes,
-            "what": "one-shot wave64 copy and read (16 B per lane, nontemporal); runtime copy = torch copy_"}
+            "what": "one-shot wave64 copy and read (16 B per lane, nontemporal) of random bytes; runtime copy = torch copy_"}
 
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
