@@ -42,6 +42,9 @@ def test_bench_prints_the_contract_line(tmp_path):
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == d["unit"]
     assert isinstance(cb["sample"], str) and cb["sample"]
+    # timed on one thread and on the process's CPU share, both stated
+    assert cb["one_thread"]["cores"] == 1 and cb["one_thread"]["value"] > 0
+    assert cb["cores"] == cb["host"]["threads"] <= cb["host"]["affinity_cores"]
     # the per-step log: one line per extra step, after everything timed
     recs = [json.loads(ln) for ln in open(log_path)]
     assert len(recs) == 3

@@ -16,7 +16,7 @@ import synth
 from gradient_reduce_adam_amd import driver
 from synth import workloads
 
-from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, ulp_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,7 @@ def test_bucketed_reduction_equals_whole_bitwise(name, two_streams):
         ref = oracle_run(w, steps)
         for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
             assert_scalars_match(g, r, where=f"{name} step {s}")
-        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+        assert_state_close(got[0], ref.state[(0, w.P)], ulp_bound(w), where=name)
 
 
 def test_shuffled_buckets_equal_whole_bitwise():
@@ -171,7 +171,7 @@ def test_bucketed_single_pass_equals_whole_bitwise(name, two_streams):
         ref = oracle_run(w, steps)
         for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
             assert_scalars_match(g, r, where=f"{name} step {s}")
-        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+        assert_state_close(got[0], ref.state[(0, w.P)], ulp_bound(w), where=name)
 
 
 def test_shuffled_single_pass_buckets_equal_whole_bitwise():
@@ -250,7 +250,7 @@ def test_bucketed_micro_steps_equal_whole_bitwise(name, two_streams):
         ref = oracle_run(w, steps)
         for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
             assert_scalars_match(g, r, where=f"{name} step {s}")
-        assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+        assert_state_close(got[0], ref.state[(0, w.P)], ulp_bound(w), where=name)
 
 
 def test_shuffled_micro_step_buckets_equal_whole_bitwise():
@@ -350,7 +350,7 @@ def test_bucketed_reduce_replicas_equals_whole_bitwise(name, src):
     ref = oracle_run(w, steps)
     for s, (g, r) in enumerate(zip(got[1], ref.scalars), start=1):
         assert_scalars_match(g, r, where=f"{name} step {s}")
-    assert_state_close(got[0], ref.state[(0, w.P)], where=name)
+    assert_state_close(got[0], ref.state[(0, w.P)], ulp_bound(w), where=name)
 
 
 def test_reduce_replicas_bucket_errors():

@@ -11,7 +11,7 @@ import torch
 import gradient_reduce_adam_amd as dp
 from synth import workloads
 
-from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, ulp_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +93,7 @@ def test_recovery_drill_resharded_bitwise(name, tmp_path):
     # the oracle's uninterrupted run agrees with the resumed one
     ref = oracle_run(w, steps)
     assert_scalars_match(whole[1], ref.scalars[-1], where=name)
-    assert_state_close(whole[0], ref.state[(0, P)], where=name)
+    assert_state_close(whole[0], ref.state[(0, P)], ulp_bound(w), where=name)
 
 
 def test_save_and_load_through_per_tensor_bindings(tmp_path):

@@ -1,10 +1,13 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (default chunk size, the fused step sequence).
 
-The oracle computes the global statistics of every step over the whole flat
-range (they decide clipping and skipping) and the update on sampled windows:
-the first and last elements, windows straddling tensor and chunk boundaries,
-windows around every injected non-finite value, and seeded random windows.
+Every workload runs for its own number of steps.  The oracle computes the
+global statistics of every step over the whole flat range (they decide
+clipping and skipping) and the update on sampled windows: the first and last
+elements, a window around every tensor boundary (224 of them in the 7B
+layout), windows straddling chunk boundaries, windows around every injected
+non-finite value, and seeded random windows.  Master, m and v must also lie
+within the ulp bound of the comparison (bit-exact without clipping).
 Two properties are checked at full size as well: the sum of squares the
 library reports is the binary64 sum of squares of its own g_bar (a torch
 reduction), and the skip flag is set exactly when that g_bar holds an inf or
@@ -17,16 +20,31 @@ import torch
 
 from synth import workloads
 
-from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, sample_windows
+from gpu_common import DeviceRun, assert_scalars_match, assert_state_close, log, oracle_run, sample_windows, ulp_bound
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-# steps per workload: every step of the workload where the oracle's full
-# statistics pass stays within tens of seconds of host time; the workloads
-# without clipping also run through the single pass, as the benchmark times
-# them (the 7B ZeRO-3 share skips its third step there too)
-CASES = [("gpt2_small", 4, False), ("zero3_rank_7b", 5, False), ("unsharded_7b", 2, False),
-         ("tp_column_slice", 1, False), ("zero3_rank_7b", 5, True), ("unsharded_7b", 2, True)]
+# every workload at its own step count; the workloads without clipping also
+# run through the single pass, as the benchmark times them (the 7B ZeRO-3
+# share skips its third step on both paths)
+CASES = [("gpt2_small", 20, False), ("zero3_rank_7b", 5, False), ("zero3_rank_7b", 5, True),
+         ("unsharded_7b", 3, False), ("unsharded_7b", 3, True), ("tp_column_slice", 3, False)]
+
+# the oracle's run of a workload, shared by its two update paths (same
+# windows, same steps): the full statistics pass is the expensive part
+_ORACLE = {}
+
+
+def _oracle(w, steps, wins):
+    key = (w.name, steps, tuple(wins))
+    if key not in _ORACLE:
+        _ORACLE.clear()
+        t0 = time.time()
+        _ORACLE[key] = oracle_run(w, steps, windows=wins, keep_gbar=(steps,),
+                                  progress=lambda s, rec: log(f"  oracle step {s}: norm {rec['norm']:.6g} "
+                                                              f"found_inf {rec['found_inf']} ({time.time() - t0:.0f} s)"))
+        log(f"  oracle done in {time.time() - t0:.1f} s")
+    return _ORACLE[key]
 
 
 def _sumsq_fp64(x: torch.Tensor) -> float:
@@ -63,19 +81,18 @@ def test_full_size_sampled_parity(name, steps, single):
         assert abs(states[-1]["sumsq"] - ss) <= 1e-12 * ss, (states[-1]["sumsq"], ss)
         assert states[-1]["found_inf"] == int(bad)
 
-    t0 = time.time()
-    ref = oracle_run(w, steps, windows=wins, keep_gbar=(steps,))
-    log(f"  oracle done in {time.time() - t0:.1f} s")
+    ref = _oracle(w, steps, wins)
+    assert len(states) == len(ref.scalars) == w.steps
     for s, (g, r) in enumerate(zip(states, ref.scalars), start=1):
         assert_scalars_match(g, r, where=f"{name} step {s}")
     worst = {}
     for win in wins:
-        rep = assert_state_close(got[win], ref.state[win], where=f"{name} window {win}")
+        rep = assert_state_close(got[win], ref.state[win], ulp_bound(w), where=f"{name} window {win}")
         for k, v in rep.items():
             worst[k] = max(worst.get(k, 0), v)
         if not single:
             assert np.array_equal(got[win]["gbar"].view(np.uint32), ref.gbar[steps][win].view(np.uint32)), win
-    log(f"  max ulp over windows: {worst}")
+    log(f"  max ulp over windows: {worst} (bound {ulp_bound(w)})")
 
 
 def _device_state(run):

@@ -12,7 +12,7 @@ import synth
 from gradient_reduce_adam_amd import driver
 from synth import workloads
 
-from gpu_common import assert_scalars_match, assert_state_close, log, oracle_run
+from gpu_common import assert_scalars_match, assert_state_close, log, oracle_run, ulp_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -97,7 +97,7 @@ def test_rebinding_pointer_tables_between_launches():
         plan.close()
     ref = oracle_run(w, w.steps)
     assert_scalars_match(state, ref.scalars[-1], where="rebound tables")
-    assert_state_close(got, ref.state[(0, P)], where="rebound tables")
+    assert_state_close(got, ref.state[(0, P)], ulp_bound(w), where="rebound tables")
 
 
 def test_shard_ranges_change_over_a_run():
@@ -129,4 +129,4 @@ def test_shard_ranges_change_over_a_run():
         d.close()
     ref = oracle_run(w, 4)
     assert_scalars_match(state, ref.scalars[-1], where="changing shards")
-    assert_state_close(got, ref.state[(0, P)], where="changing shards")
+    assert_state_close(got, ref.state[(0, P)], ulp_bound(w), where="changing shards")
