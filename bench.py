@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 RESIDENT_GRAD_BUDGET = 80e9  # bytes of pre-generated gradients kept in HBM
-CPU_BASELINE_SECONDS = 10.0  # oracle work timed for the CPU baseline
+CPU_BASELINE_SECONDS = 10.0  # oracle work timed for each leg of the CPU baseline
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = (os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip"),
               os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "dp_internal.h"))
@@ -40,9 +40,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="gpt2_small",
+    ap.add_argument("--workload", default="unsharded_7b",
                     help="tiny | gpt2_small | zero3_rank_7b | unsharded_7b | tp_column_slice")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24, help="params in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26, help="params in the oracle's timed sample")
+    ap.add_argument("--zero3-placements", type=int, default=3, metavar="K",
+                    help="with the default workload: also time the ZeRO-3 rank share's single pass in this process "
+                         "at K HBM placements (its state allocated behind spacers of 0, 3, 6, ... GiB) and report "
+                         "the median and the range as an extra key; 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
     ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
@@ -292,13 +296,15 @@ def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
             ckpt_dir: str = "", state: str = "hbm", graph: bool = False, offload: str = "direct",
-            layout: str = "auto", log_path: str = ""):
+            layout: str = "auto", log_path: str = "", spacer: int = 0):
     import torch
 
     import synth
     from gradient_reduce_adam_amd import DP_ROLE_GRAD, dp_plan_bind_flat, driver
 
     torch.cuda.set_device(0)
+    # an allocation held ahead of the state moves the state to other HBM pages
+    spacer_buf = torch.empty(spacer, dtype=torch.uint8, device="cuda") if spacer else None
     if calib:
         src = torch.empty(calib, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -454,7 +460,7 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         per_kind[kind] = {"launches": len(ms), "avg_ms": sum(ms) / len(ms), "total_ms": sum(ms)}
     used_layout = d.layout
     d.close()
-    del bufs
+    del bufs, ring, spacer_buf
     torch.cuda.empty_cache()
     per_kind["skipped_step_ms"] = skipped_ms
     per_kind["step_ms"] = None if graph else step_ms  # the eager steps; a graph replays them as one
@@ -593,39 +599,108 @@ def device_info() -> dict:
     return info
 
 
-def cpu_baseline(w, sample: int) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload: one
-    full step (all micro-steps, reduction, statistics, update) over `sample`
-    parameters in one tensor, gradients generated beforehand (not timed)."""
-    import numpy as np
+def cpu_share() -> dict:
+    """The host threads this process may use: the cores of its affinity mask,
+    capped by a cgroup CPU quota and by OMP_NUM_THREADS where either is set
+    (a machine shared between GPUs gives each GPU's jobs a share of its
+    cores)."""
+    affinity = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, int(math.ceil(int(q) / int(period))))
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    omp_n = int(omp) if omp.isdigit() and int(omp) > 0 else None
+    share = min(x for x in (affinity, quota, omp_n) if x is not None)
+    return {"affinity_cores": affinity, "cgroup_quota_cores": quota, "omp_num_threads": omp_n, "threads": share}
 
+
+def cpu_baseline(w, sample: int) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole steps (every micro-step, the replica tree, the statistics and the
+    update) over `sample` parameters in one tensor, on one batch of gradients
+    generated beforehand (not timed).  Timed twice: on one thread, and on
+    every thread of the process's CPU share; each leg repeats steps until
+    about CPU_BASELINE_SECONDS of oracle work are timed.  The oracle's driver
+    spreads the accumulation, the replica tree and the statistics over its
+    threads and runs the update of a window on one, so the second leg gains
+    on the first only in those parts."""
     import oracle
     import synth
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    share = cpu_share()
+    gen_threads = share["threads"]
     ws = w.with_(numel=(sample,), injections=(), scaled_tensors=())
     calls = [(r, 1) for r in range(ws.n)] if ws.partials else [(r, k) for k in range(1, ws.a + 1) for r in range(ws.n)]
     scale = ws.init_scale if ws.scaler != "none" else 1.0
-    pre = {rk: synth.grad_host(ws, 1, rk[0], rk[1], 0, sample, scale, threads=threads) for rk in calls}
-    master = synth.master_host(ws, 0, sample, threads=threads)
+    pre = {rk: synth.grad_host(ws, 1, rk[0], rk[1], 0, sample, scale, threads=gen_threads) for rk in calls}
+    master = synth.master_host(ws, 0, sample, threads=gen_threads)
 
     def grad_fn(step, r, k, lo, hi, sc):
         return pre[(r, k)][lo:hi]
 
-    # one untimed step, then runs of steps (the same batch each step) until
-    # about ten seconds of oracle work are timed
-    oracle.run(ws, 1, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
-    steps, dt, k = 0, 0.0, 1
-    while dt < CPU_BASELINE_SECONDS:
-        t0 = time.perf_counter()
-        oracle.run(ws, k, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
-        dt += time.perf_counter() - t0
-        steps += k
-        k = max(1, min(200, int(math.ceil((CPU_BASELINE_SECONDS - dt) * steps / dt))))
-    return {"value": sample * steps / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps} full steps of {ws.name} (n={ws.n}, a={ws.a}, every micro-step, the replica tree, "
-                      f"statistics and update) over {sample} params in one tensor, one pre-generated batch, "
-                      f"{dt:.1f} s"}
+    def leg(threads: int) -> dict:
+        # runs of steps until the time is reached
+        steps, dt, k = 0, 0.0, 1
+        while dt < CPU_BASELINE_SECONDS:
+            t0 = time.perf_counter()
+            oracle.run(ws, k, grad_fn, lambda lo, hi: master[lo:hi], threads=threads, chunk=1 << 18)
+            dt += time.perf_counter() - t0
+            steps += k
+            k = max(1, min(200, int(math.ceil((CPU_BASELINE_SECONDS - dt) * steps / dt))))
+        return {"value": sample * steps / dt, "cores": threads, "steps": steps, "seconds": dt}
+
+    # one untimed step first (pages of the inputs and the state touched once)
+    oracle.run(ws, 1, grad_fn, lambda lo, hi: master[lo:hi], threads=gen_threads, chunk=1 << 18)
+    one = leg(1)
+    many = leg(gen_threads) if gen_threads > 1 else one
+    return {"value": many["value"], "unit": "params/s", "cores": many["cores"], "kind": "oracle",
+            "sample": f"{many['steps']} full steps of {ws.name} (n={ws.n}, a={ws.a}: every micro-step, the replica "
+                      f"tree, statistics and update) over {sample} params in one tensor on one pre-generated batch, "
+                      f"{many['seconds']:.1f} s on {many['cores']} threads; the same on 1 thread: {one['steps']} "
+                      f"steps in {one['seconds']:.1f} s",
+            "one_thread": {"value": one["value"], "unit": "params/s", "cores": 1, "steps": one["steps"],
+                           "seconds": one["seconds"]},
+            "host": share}
+
+
+def zero3_single_pass(steps: int, warmup: int, placements: int) -> dict:
+    """The ZeRO-3 rank share's single pass (8 incoming bf16 partials, dynamic
+    loss scale) timed in this process at several HBM placements: its arrays
+    allocated behind a spacer of 0, 3, 6, ... GiB.  Its bandwidth depends on
+    where its 15 concurrent streams land in physical memory, so one placement
+    is not its figure: the median and the range are."""
+    from synth import workloads
+
+    w = workloads.by_name("zero3_rank_7b")
+    per_param = bytes_model(w, True)
+    runs = []
+    for k in range(placements):
+        elapsed, per_kind, state, _, _ = run_gpu(w, steps, warmup, single=True, spacer=k * (3 << 30))
+        ms = elapsed * 1e3 / steps
+        k_ms = per_kind["reduce_adamw"]["avg_ms"]
+        k_gbps = launch_bytes(w, "reduce_adamw", True) / (k_ms * 1e-3) / 1e9
+        runs.append({"spacer_gib": 3 * k, "ms_per_step": ms, "params_per_s": w.P / (ms * 1e-3),
+                     "hbm_gbps": sum(per_param.values()) * w.P / (ms * 1e-3) / 1e9,
+                     "reduce_adamw_ms": k_ms, "reduce_adamw_gbps": k_gbps, "frac": k_gbps / PEAK_HBM_GBPS,
+                     "skipped_step_ms": per_kind.get("skipped_step_ms")})
+    fr = sorted(r["frac"] for r in runs)
+    med = statistics.median(r["ms_per_step"] for r in runs)
+    return {"workload": w.name, "params": w.P, "update": "single-pass", "steps": steps,
+            "bytes_per_param_step": sum(per_param.values()),
+            "ms_per_step_median": med, "params_per_s_median": w.P / (med * 1e-3),
+            "hbm_gbps_median": sum(per_param.values()) * w.P / (med * 1e-3) / 1e9,
+            "reduce_adamw_frac_median": statistics.median(fr), "reduce_adamw_frac_range": [fr[0], fr[-1]],
+            "placements": runs}
+
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON line is the only stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -654,6 +729,7 @@ def main():
                                 args.tokens, single, args.micro_buckets):
             print(json.dumps(line), flush=True)
         return
+    progress(f"{w.name}: {args.warmup} warm-up and {args.steps} timed steps ({'single' if single else 'two'}-pass)")
     elapsed, per_kind, state, ckpt, layout = run_gpu(w, args.steps, args.warmup, args.chunk, args.copy_calibration,
                                                      args.bind, single, args.checkpoint_dir, args.state, args.graph,
                                                      args.offload, args.layout, args.log_steps)
@@ -676,6 +752,7 @@ def main():
         ent = t.get(w.name, {}).get(dom)
         if ent and ent.get("kernel_source_sha") == kernel_source_hash():
             traffic = ent["bytes_per_launch"]
+    progress("measured ceilings (copy and read of random bytes)")
 
     line = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per full DP step",
@@ -704,7 +781,11 @@ def main():
         "unfused_equiv_gbps": unfused_bytes_per_param(w) * w.P / (ms_per_step * 1e-3) / 1e9,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "bytes_per_launch": dom_bytes,
-                     "avg_launch_ms": dom_ms},
+                     "avg_launch_ms": dom_ms,
+                     "traffic_source": ("FETCH_SIZE + WRITE_SIZE per launch from a separate rocprofv3 --pmc run of "
+                                        "this workload (profiles/traffic.json), scaled by the same counters on a "
+                                        "plain copy; valid for the kernel source it was taken on (hash checked)"
+                                        if traffic is not None else None)},
         "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
         "skipped_step_ms": skipped_ms,
@@ -729,7 +810,11 @@ def main():
                             "peak": PEAK_PCIE_GBPS, "unit": "GB/s",
                             "frac": 24.0 * w.P / (upd_ms * 1e-3) / 1e9 / PEAK_PCIE_GBPS, "traffic": None,
                             "bytes_per_launch": 24.0 * w.P, "avg_launch_ms": upd_ms}
+    if w.name == "unsharded_7b" and args.zero3_placements > 0 and args.state == "hbm" and not args.graph:
+        progress(f"ZeRO-3 rank share, single pass, {args.zero3_placements} placements")
+        line["zero3_rank_7b_single_pass"] = zero3_single_pass(args.steps, args.warmup, args.zero3_placements)
     if not args.no_cpu_baseline:
+        progress(f"CPU baseline: the oracle on {args.cpu_sample} params of {w.name}")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
     print(json.dumps(line), flush=True)
     if ckpt:
