@@ -30,6 +30,8 @@ DP_F32, DP_F16, DP_BF16 = 0, 1, 2
 DP_SCALER_NONE, DP_SCALER_STATIC, DP_SCALER_DYNAMIC = 0, 1, 2
 DP_MAX_REPLICAS = 16
 DP_DEFAULT_CHUNK = 16384
+DP_STATIC_MAX_PARAMS = 1 << 30
+DP_STATIC_SCRATCH_BYTES = 51920896
 
 DTYPES = {"f32": DP_F32, "f16": DP_F16, "bf16": DP_BF16}
 SCALERS = {"none": DP_SCALER_NONE, "static": DP_SCALER_STATIC, "dynamic": DP_SCALER_DYNAMIC}
@@ -41,7 +43,7 @@ EXPORTS = ("dp_abi_version", "dp_status_string", "dp_last_error", "dp_plan_creat
            "dp_plan_info_get", "dp_plan_chunks", "dp_plan_bind_flat", "dp_plan_bind_tensors",
            "dp_plan_prepare_range", "dp_plan_drop_ranges", "dp_state_init", "dp_accumulate", "dp_accumulate_all",
            "dp_accumulate_all_range", "dp_accumulate_reduce", "dp_accumulate_reduce_range",
-           "dp_reduce_replicas", "dp_reduce_replicas_range", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_range",
+           "dp_reduce_replicas", "dp_reduce_replicas_range", "dp_grad_stats", "dp_adam_step", "dp_reduce_adam_step", "dp_reduce_adam_step_noalloc", "dp_reduce_adam_range",
            "dp_reduce_adam_finish", "dp_read_state",
            "dp_ckpt_write_shard", "dp_ckpt_commit", "dp_ckpt_read", "dp_checkpoint_save", "dp_checkpoint_commit",
            "dp_checkpoint_load")
@@ -156,6 +158,9 @@ def _load():
         "dp_grad_stats": (ctypes.c_int, [vp, i32, dbl, vp]),
         "dp_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
         "dp_reduce_adam_step": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), vp]),
+        "dp_reduce_adam_step_noalloc": (ctypes.c_int, [i64, i32, ctypes.c_int, ctypes.c_int, PP, PP, PP, PP, PP, vp,
+                                                       vp, ctypes.POINTER(StateCfg), ctypes.POINTER(AdamHparams),
+                                                       vp]),
         "dp_reduce_adam_range": (ctypes.c_int, [vp, ctypes.POINTER(AdamHparams), i64, i64, vp]),
         "dp_reduce_adam_finish": (ctypes.c_int, [vp, vp]),
         "dp_read_state": (ctypes.c_int, [vp, ctypes.POINTER(StepState), vp]),
@@ -321,6 +326,29 @@ def dp_adam_step(plan: int, lr: float, eps: float, weight_decay: float, shard_be
 def dp_reduce_adam_step(plan: int, lr: float, eps: float, weight_decay: float, stream=None) -> None:
     hp = AdamHparams(lr, eps, weight_decay)
     _check(lib.dp_reduce_adam_step(ctypes.c_void_p(plan), ctypes.byref(hp), ctypes.c_void_p(_stream(stream))))
+
+
+def dp_reduce_adam_step_noalloc(P: int, n: int, grad_dtype: str, param_dtype: str, grads: Sequence, accs,
+                                master: Sequence, exp_avg: Sequence, exp_avg_sq: Sequence, param, state,
+                                lr: float, eps: float, weight_decay: float, beta1: float, beta2: float,
+                                scaler: str = "none", init_scale: float = 1.0, backoff: float = 0.5,
+                                growth: float = 2.0, growth_interval: int = 2000, stream=None) -> None:
+    """grads: n device buffers (tensors or addresses); accs: n buffers or
+    None; master, exp_avg, exp_avg_sq: the two banks of each; state: device
+    memory holding a dp_step_state."""
+    def arr(xs):
+        return (ctypes.c_void_p * max(1, len(xs)))(*[_addr(x) for x in xs])
+
+    g = arr(list(grads))
+    a = arr(list(accs)) if accs is not None else None
+    banks = [arr(list(x)) for x in (master, exp_avg, exp_avg_sq)]
+    cfg = StateCfg(beta1, beta2, SCALERS[scaler], growth_interval, init_scale, backoff, growth)
+    hp = AdamHparams(lr, eps, weight_decay)
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    _check(lib.dp_reduce_adam_step_noalloc(P, n, DTYPES[grad_dtype], DTYPES[param_dtype], g,
+                                           a if a is not None else ctypes.cast(None, pp), *banks,
+                                           ctypes.c_void_p(_addr(param)), ctypes.c_void_p(_addr(state)),
+                                           ctypes.byref(cfg), ctypes.byref(hp), ctypes.c_void_p(_stream(stream))))
 
 
 def dp_reduce_adam_range(plan: int, lr: float, eps: float, weight_decay: float, begin: int, end: int,

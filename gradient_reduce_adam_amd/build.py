@@ -27,7 +27,7 @@ def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "csrc")
     inc = ["-I", os.path.join(ROOT, "include"), "-I", src]
     objs = []
-    for name in ("kernels.hip", "api.cpp", "checkpoint.cpp"):
+    for name in ("kernels.hip", "api.cpp", "checkpoint.cpp", "noalloc.hip"):
         obj = os.path.join(src, name + ".o")
         out = _run(["hipcc", *HIP_FLAGS, *inc, "-c", os.path.join(src, name), "-o", obj])
         if verbose and out:

@@ -125,5 +125,10 @@ hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int 
 hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& s, RoleRef p, const DevState* st,
                                 hipStream_t stream);
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t stream);
+// The chunk table of one tensor [0, P) (chunks of 2^log2c elements) into
+// device memory `chunks`, and zeros in the statistics slots that no piece of
+// its npieces maps to (the fold adds them).
+hipError_t launch_flat_table(dp_chunk* chunks, int64_t P, int log2c, StatsBuf sb, int64_t npieces,
+                             hipStream_t stream);
 
 }  // namespace dpk

@@ -665,6 +665,29 @@ __global__ void __launch_bounds__(kWave) k_restore_param(Table t, StateRefs sr, 
     }
 }
 
+// The chunk table of one tensor of P elements, [0, P) in chunks of 2^log2c
+// elements, written into caller-provided device memory; and zeros in the
+// statistics slots that no piece of that table maps to.  Those slots are the
+// ones of pieces [npieces, 8 ceil(npieces / 8)): a fold adds them, and memory
+// that an earlier call with another size used may hold other values there.
+__global__ void __launch_bounds__(256) k_flat_table(dp_chunk* __restrict__ chunks, int64_t P, int log2c,
+                                                      int64_t nchunks, StatsBuf sb, int64_t npieces) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < nchunks) {
+        const int64_t flat = i << log2c;
+        const int64_t rest = P - flat;
+        const int64_t c = int64_t{1} << log2c;
+        chunks[i] = dp_chunk{flat, flat, 0, static_cast<int32_t>(rest < c ? rest : c)};
+    }
+    const int64_t per = (npieces + 7) >> 3;
+    const int64_t p = npieces + i;
+    if (p < 8 * per) {
+        const int64_t slot = (p & 7) * per + (p >> 3);
+        sb.sumsq[slot] = 0.0;
+        sb.bad[slot] = 0;
+    }
+}
+
 // ---- launch helpers ---------------------------------------------------------
 // Launches `launch(base, grid)` over pieces [p0, p1), one workgroup each, in
 // slices of at most kMaxBlocksPerLaunch (gridDim.y = ny); base is the piece
@@ -872,6 +895,14 @@ hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& s
         if (pdt == DP_BF16) hipLaunchKernelGGL((k_restore_param<false, 2>), grid, dim3(kWave), 0, s, t, sr, p, st);
         else hipLaunchKernelGGL((k_restore_param<false, 1>), grid, dim3(kWave), 0, s, t, sr, p, st);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_flat_table(dp_chunk* chunks, int64_t P, int log2c, StatsBuf sb, int64_t npieces, hipStream_t s) {
+    const int64_t nchunks = (P + (int64_t{1} << log2c) - 1) >> log2c;
+    const int64_t work = nchunks > 8 ? nchunks : 8;
+    hipLaunchKernelGGL(k_flat_table, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, chunks, P,
+                       log2c, nchunks, sb, npieces);
     return hipGetLastError();
 }
 

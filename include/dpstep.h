@@ -52,9 +52,13 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 2
+#define DP_ABI_VERSION 3
 #define DP_MAX_REPLICAS 16
 #define DP_DEFAULT_CHUNK 16384
+/* dp_reduce_adam_step_noalloc: the largest flat space it takes, and the bytes
+ * of the static device array that holds its scratch on each GPU. */
+#define DP_STATIC_MAX_PARAMS (INT64_C(1) << 30)
+#define DP_STATIC_SCRATCH_BYTES 51920896
 
 typedef enum dp_status {
     DP_OK = 0,
@@ -353,6 +357,49 @@ dp_status dp_adam_step(dp_plan* plan, const dp_adam_hparams* hp, int64_t shard_b
  * dp_state_init.  Afterwards dp_adam_step returns DP_ERR_STATE until the next
  * step's statistics. */
 dp_status dp_reduce_adam_step(dp_plan* plan, const dp_adam_hparams* hp, hipStream_t stream);
+
+/* For callers that cannot allocate device memory -- work recorded under HIP
+ * graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc: dp_reduce_adam_step for a plan of one tensor of P elements with
+ * every role bound flat and the default chunk size, without a plan.  Nothing
+ * is allocated.  The scratch the kernels need (statistics slots, the fold's
+ * second level, the chunk table) is one static device array of
+ * DP_STATIC_SCRATCH_BYTES (49.5 MiB) that each GPU holds from the library's
+ * first use there until the process ends; P may not exceed
+ * DP_STATIC_MAX_PARAMS (2^30; DP_ERR_INVALID_ARG beyond).
+ *
+ * The caller passes every input and output:
+ *  - grads: host array [n] of device pointers, replica r's last micro-step
+ *    (or incoming partial) in the grad dtype, P elements each;
+ *  - accs: host array [n] of device pointers to binary32 accumulators that
+ *    hold the sum of the earlier micro-steps (read, not written), or NULL when
+ *    there were none;
+ *  - master, exp_avg, exp_avg_sq: host arrays [2] of device pointers, the two
+ *    binary32 banks of each; param: device, P elements of the param dtype;
+ *  - state: device memory holding a dp_step_state (8-byte aligned), read and
+ *    written.  The caller sets it up once, for example by copying a host
+ *    struct with t = iter = growth_tracker = 0, beta1_pow = beta2_pow = 1,
+ *    scale = the initial loss scale (1 without a scaler), bank = 0 and
+ *    found_inf = 0; state->bank then says which bank is current;
+ *  - cfg: the scaler and the betas, as for dp_state_init; hp as for
+ *    dp_reduce_adam_step.
+ *
+ * The result, the two banks, the parameters and the state block, equals bit
+ * for bit what dp_reduce_adam_step leaves on such a plan in the same state.
+ * On a skipped step the current bank stays current and PARAM is emitted
+ * again from it.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind.  The call clears what has to start at zero itself, but calls that
+ * overlap on one GPU (on different streams, or from different threads) race
+ * on the array and give wrong results.  The first call on each device
+ * resolves the array's device address (hipGetSymbolAddress): make it outside
+ * graph capture.  Asynchronous on stream. */
+dp_status dp_reduce_adam_step_noalloc(int64_t P, int32_t n, dp_dtype grad_dtype, dp_dtype param_dtype,
+                                      void* const* grads, void* const* accs, void* const* master,
+                                      void* const* exp_avg, void* const* exp_avg_sq, void* param,
+                                      dp_step_state* state, const dp_state_cfg* cfg, const dp_adam_hparams* hp,
+                                      hipStream_t stream);
 
 /* dp_reduce_adam_step in buckets: the single pass over one bucket [begin,
  * end) of the flat space, so the update of the parameters whose gradients

@@ -23,14 +23,14 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     assert sorted(dp.EXPORTS) == names
     for n in names:
         assert hasattr(dp.lib, n), n
 
 
 def test_abi_version_and_status_strings():
-    assert dp.dp_abi_version() == 2
+    assert dp.dp_abi_version() == 3
     assert dp.dp_status_string(dp.DP_ERR_RANGE) == "range out of bounds"
     assert dp.dp_status_string(0) == "ok"
     # every status has a string in the library and a name in the binding
@@ -264,3 +264,26 @@ def test_headers_are_c_and_host_calls_work_from_c(tmp_path):
     (tmp_path / "ckpt").mkdir()
     r = subprocess.run([str(exe), str(tmp_path / "ckpt")], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("P", [-1, dp.DP_STATIC_MAX_PARAMS + 1, 1 << 40])
+def test_noalloc_rejects_sizes_outside_its_scratch(P):
+    """The allocation-free single pass checks the size against its static
+    scratch before it touches a GPU (the addresses are never used)."""
+    fake = 1 << 20
+    with pytest.raises(dp.DpError) as e:
+        dp.dp_reduce_adam_step_noalloc(P, 1, "bf16", "bf16", [fake], None, [fake, fake], [fake, fake],
+                                       [fake, fake], fake, fake, 1e-3, 1e-8, 0.01, 0.9, 0.999, stream=0)
+    assert e.value.status == dp.DP_ERR_INVALID_ARG
+    if P > 0:
+        assert "DP_STATIC_MAX_PARAMS" in e.value.message
+
+
+def test_noalloc_scratch_size_matches_its_layout():
+    """The header's scratch size is the sum of its parts for 2^30 elements:
+    binary64 sums and 32-bit counts per 256-element piece, binary64 sums and
+    64-bit counts per 4096 pieces, and one 24-byte chunk entry per 16384
+    elements."""
+    pieces = dp.DP_STATIC_MAX_PARAMS // 256
+    assert dp.DP_STATIC_SCRATCH_BYTES == pieces * 12 + (pieces // 4096) * 16 + \
+        (dp.DP_STATIC_MAX_PARAMS // dp.DP_DEFAULT_CHUNK) * 24
