@@ -166,6 +166,8 @@ const Binding* gbar_binding(const dp_plan* p) {
     return b;
 }
 
+Binding* gbar_binding(dp_plan* p) { return const_cast<Binding*>(gbar_binding(static_cast<const dp_plan*>(p))); }
+
 dp_status need(const Binding* b, const char* what) {
     if (!b->bound) return fail(DP_ERR_UNBOUND, "role %s is not bound", what);
     return DP_OK;
@@ -264,6 +266,176 @@ dp_status bucket_span(dp_plan* p, int64_t begin, int64_t end, int64_t* p0, int64
     return DP_OK;
 }
 
+// ---- per-tensor pointer tables: the ring of device slots -------------------
+// The bindings one launch reads; the per-tensor ones among them get their
+// pending upload before the launch and an event behind it.
+constexpr int kMaxReads = dpk::kMaxUploads;
+struct Reads {
+    Binding* b[kMaxReads];
+    int n = 0;
+    void add(Binding* x) {
+        if (n < kMaxReads) b[n++] = x;
+    }
+    void replicas(dp_plan* p, dp_role role) {
+        for (int32_t r = 0; r < p->n; ++r) add(&p->roles[role][r]);
+    }
+    void state(dp_plan* p) {
+        for (int role = DP_ROLE_MASTER; role <= DP_ROLE_EXP_AVG_SQ; ++role)
+            for (int bank = 0; bank < 2; ++bank) add(&p->roles[role][bank]);
+    }
+};
+
+// The plan's shared events (EventPool).
+hipError_t ev_take(dp_plan* p, int* out) {
+    dpapi::EventPool& pool = p->events;
+    if (!pool.free_list.empty()) {
+        *out = pool.free_list.back();
+        pool.free_list.pop_back();
+        return hipSuccess;
+    }
+    hipEvent_t e = nullptr;
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) return r;
+    pool.ev.push_back(e);
+    pool.refs.push_back(0);
+    *out = static_cast<int>(pool.ev.size()) - 1;
+    return hipSuccess;
+}
+
+void ev_ref(dp_plan* p, int i) { ++p->events.refs[i]; }
+
+void ev_unref(dp_plan* p, int i) {
+    if (i < 0) return;
+    if (--p->events.refs[i] == 0) p->events.free_list.push_back(i);
+}
+
+// Before a launch on `stream`: upload every per-tensor table that a
+// rebinding left pending (one kernel for all of them, one event behind it),
+// and make the stream wait for uploads issued on other streams.
+dp_status stage_tables(dp_plan* p, const Reads& rd, hipStream_t stream) {
+    const int32_t T = p->T;
+    if (T == 0) return DP_OK;
+    dpk::TableUploads up{};
+    up.T = T;
+    Binding* pend[dpk::kMaxUploads];
+    for (int i = 0; i < rd.n; ++i) {
+        Binding& b = *rd.b[i];
+        if (!b.bound || !b.dev_table) continue;
+        const int k = b.slot;
+        if (b.pending) {
+            bool seen = false;  // a binding listed twice is uploaded once
+            for (int j = 0; j < up.count; ++j) seen = seen || pend[j] == &b;
+            if (seen) continue;
+            up.src[up.count] = b.ring_host_dev + static_cast<size_t>(k) * T;
+            up.dst[up.count] = b.dev_table;
+            pend[up.count++] = &b;
+        } else if (b.upload_stream[k] != stream && b.uploaded[k] >= 0) {
+            hipError_t e = hipStreamWaitEvent(stream, p->events.ev[b.uploaded[k]], 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent on a pointer table's upload");
+        }
+    }
+    if (up.count == 0) return DP_OK;
+    hipError_t e = dpk::launch_upload_tables(up, stream);
+    if (e != hipSuccess) return hip_fail(e, "upload of rebound pointer tables");
+    int ev = -1;
+    e = ev_take(p, &ev);
+    if (e == hipSuccess) e = hipEventRecord(p->events.ev[ev], stream);
+    if (e != hipSuccess) {
+        if (ev >= 0 && p->events.refs[ev] == 0) p->events.free_list.push_back(ev);
+        return hip_fail(e, "event behind a pointer table upload");
+    }
+    for (int j = 0; j < up.count; ++j) {
+        Binding& b = *pend[j];
+        const int k = b.slot;
+        ev_unref(p, b.uploaded[k]);
+        b.uploaded[k] = ev;
+        ev_ref(p, ev);
+        b.upload_stream[k] = stream;
+        b.pending = false;
+    }
+    return DP_OK;
+}
+
+// After a launch on `stream`: one event behind it, held by every per-tensor
+// table slot the launch read.
+dp_status note_reads(dp_plan* p, const Reads& rd, hipStream_t stream) {
+    bool any = false;
+    for (int i = 0; i < rd.n && !any; ++i) any = rd.b[i]->bound && rd.b[i]->dev_table;
+    if (!any) return DP_OK;
+    int ev = -1;
+    hipError_t e = ev_take(p, &ev);
+    if (e == hipSuccess) e = hipEventRecord(p->events.ev[ev], stream);
+    if (e != hipSuccess) {
+        if (ev >= 0 && p->events.refs[ev] == 0) p->events.free_list.push_back(ev);
+        return hip_fail(e, "event behind a launch");
+    }
+    for (int i = 0; i < rd.n; ++i) {
+        Binding& b = *rd.b[i];
+        if (!b.bound || !b.dev_table) continue;
+        auto& uses = b.uses[b.slot];
+        bool found = false;
+        for (auto& u : uses)
+            if (u.first == stream) {
+                found = true;
+                if (u.second != ev) {
+                    ev_unref(p, u.second);
+                    u.second = ev;
+                    ev_ref(p, ev);
+                }
+            }
+        if (!found) {
+            uses.emplace_back(stream, ev);
+            ev_ref(p, ev);
+        }
+    }
+    return DP_OK;
+}
+
+// The sources of a replica reduction in `mode`, and g_bar.
+Reads reduction_reads(dp_plan* p, dpk::ReduceMode mode) {
+    Reads rd;
+    if (mode != dpk::ReduceMode::kGradients) rd.replicas(p, DP_ROLE_ACC);
+    if (mode != dpk::ReduceMode::kAccumulators) rd.replicas(p, DP_ROLE_GRAD);
+    rd.add(gbar_binding(p));
+    return rd;
+}
+
+// A launch that reads per-tensor tables: stage them, launch, note the reads.
+template <typename F>
+dp_status with_tables(dp_plan* p, const Reads& rd, hipStream_t stream, const char* what, F&& launch) {
+    dp_status s = stage_tables(p, rd, stream);
+    if (s != DP_OK) return s;
+    s = check_launch(launch(), what);
+    if (s != DP_OK) return s;
+    return note_reads(p, rd, stream);
+}
+
+// Slot k may be written again once its upload and every launch that read it
+// have finished (waits only when kRingSlots rebindings are still in flight).
+dp_status release_slot(dp_plan* p, Binding& b, int k) {
+    hipError_t e = hipSuccess;
+    if (b.uploaded[k] >= 0) {
+        e = hipEventSynchronize(p->events.ev[b.uploaded[k]]);
+        ev_unref(p, b.uploaded[k]);
+        b.uploaded[k] = -1;
+    }
+    for (auto& u : b.uses[k]) {
+        if (e == hipSuccess) e = hipEventSynchronize(p->events.ev[u.second]);
+        ev_unref(p, u.second);
+    }
+    b.uses[k].clear();
+    b.upload_stream[k] = nullptr;
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize before reusing a pointer table slot");
+    return DP_OK;
+}
+
+void free_ring(Binding& b) {
+    if (b.ring_dev) (void)hipFree(b.ring_dev);
+    if (b.ring_host) (void)hipHostFree(b.ring_host);
+    b.ring_dev = nullptr;
+    b.ring_host = nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,8 +509,8 @@ dp_status dp_plan_destroy(dp_plan* p) {
                               hipSetDevice(p->device) == hipSuccess;
         (void)hipDeviceSynchronize();
         for (auto& row : p->roles)
-            for (auto& b : row)
-                if (b.dev_table) (void)hipFree(b.dev_table);
+            for (auto& b : row) free_ring(b);
+        for (hipEvent_t ev : p->events.ev) (void)hipEventDestroy(ev);
         if (p->full.dev) (void)hipFree(p->full.dev);
         for (auto& t : p->ranges)
             if (t.dev) (void)hipFree(t.dev);
@@ -408,10 +580,8 @@ dp_status dp_plan_bind_flat(dp_plan* p, dp_role role, int32_t replica, void* bas
     Binding& b = p->roles[role][replica];
     b.flat = base;
     b.tensors.clear();
-    if (b.dev_table) {
-        (void)hipFree(b.dev_table);
-        b.dev_table = nullptr;
-    }
+    b.dev_table = nullptr;  // the ring stays for a later per-tensor binding
+    b.pending = false;
     b.bound = true;
     return DP_OK;
 }
@@ -425,25 +595,40 @@ dp_status dp_plan_bind_tensors(dp_plan* p, dp_role role, int32_t replica, void* 
     s = ensure_device(p);
     if (s != DP_OK) return s;
     Binding& b = p->roles[role][replica];
-    if (b.dev_table) {
-        // the table is rewritten in place: kernels launched with the old
-        // binding, on any stream, must be done with it
-        hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before rebinding a pointer table");
-    } else if (p->T > 0) {
-        hipError_t e = hipMalloc(reinterpret_cast<void**>(&b.dev_table), sizeof(void*) * p->T);
-        if (e != hipSuccess) return fail(DP_ERR_OOM, "hipMalloc of a pointer table: %s", hipGetErrorString(e));
+    const size_t T = static_cast<size_t>(p->T);
+    if (T == 0) {
+        b.flat = nullptr;
+        b.tensors.clear();
+        b.dev_table = nullptr;
+        b.bound = true;
+        return DP_OK;
     }
-    b.tensors.assign(ptrs, ptrs + p->T);
-    b.flat = nullptr;
-    if (p->T > 0) {
-        hipError_t e = hipMemcpy(b.dev_table, b.tensors.data(), sizeof(void*) * p->T, hipMemcpyHostToDevice);
+    // the same pointers as the current table: nothing to do
+    if (b.bound && b.dev_table && std::equal(b.tensors.begin(), b.tensors.end(), ptrs)) return DP_OK;
+    if (!b.ring_dev) {  // first per-tensor binding of this role: the ring's memory
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&b.ring_dev), sizeof(void*) * T * dpapi::kRingSlots);
+        if (e == hipSuccess)
+            e = hipHostMalloc(reinterpret_cast<void**>(&b.ring_host), sizeof(void*) * T * dpapi::kRingSlots,
+                              hipHostMallocDefault);
+        if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&b.ring_host_dev), b.ring_host, 0);
         if (e != hipSuccess) {
-            b.bound = false;  // the device table is not what the host holds
-            b.tensors.clear();
-            return hip_fail(e, "hipMemcpy of a pointer table");
+            if (b.ring_dev) (void)hipFree(b.ring_dev);
+            if (b.ring_host) (void)hipHostFree(b.ring_host);
+            b.ring_dev = nullptr;
+            b.ring_host = nullptr;
+            b.ring_host_dev = nullptr;
+            return fail(DP_ERR_OOM, "allocation of a pointer table ring: %s", hipGetErrorString(e));
         }
     }
+    const int k = (b.slot + 1) % dpapi::kRingSlots;
+    s = release_slot(p, b, k);
+    if (s != DP_OK) return s;
+    std::copy(ptrs, ptrs + T, b.ring_host + k * T);
+    b.slot = k;
+    b.pending = true;
+    b.dev_table = b.ring_dev + k * T;
+    b.tensors.assign(ptrs, ptrs + T);
+    b.flat = nullptr;
     b.bound = true;
     return DP_OK;
 }
@@ -557,9 +742,12 @@ dp_status dp_accumulate(dp_plan* p, int32_t replica, int32_t first, int32_t emit
     if (s != DP_OK) return s;
     const dpk::Table t = p->full.table(first && !emit_stats && all_flat({g.ref(), a.ref()}));
     if (t.npieces > 0) {
-        s = check_launch(dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, t, g.ref(), a.ref(), p->stats,
-                                                stream),
-                         "accumulate launch");
+        Reads rd;
+        rd.add(&p->roles[DP_ROLE_GRAD][replica]);
+        rd.add(&p->roles[DP_ROLE_ACC][replica]);
+        s = with_tables(p, rd, stream, "accumulate launch", [&] {
+            return dpk::launch_accumulate(p->gdt, first != 0, emit_stats != 0, t, g.ref(), a.ref(), p->stats, stream);
+        });
         if (s != DP_OK) return s;
     }
     p->micro[replica] = first ? 1 : p->micro[replica] + 1;
@@ -587,9 +775,10 @@ static dp_status reduce_common(dp_plan* p, dpk::ReduceMode mode, const dpk::Srcs
     if (s != DP_OK) return s;
     const dpk::Table t = p->full.table(false);  // statistics: table pieces
     if (t.npieces > 0) {
-        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{0, t.npieces}, accs, grads,
-                                            gb->ref(), p->stats, stream),
-                         "reduce launch");
+        s = with_tables(p, reduction_reads(p, mode), stream, "reduce launch", [&] {
+            return dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{0, t.npieces}, accs, grads, gb->ref(),
+                                      p->stats, stream);
+        });
         if (s != DP_OK) return s;
     }
     std::fill(p->micro.begin(), p->micro.end(), 0);
@@ -645,9 +834,13 @@ dp_status dp_accumulate_all(dp_plan* p, int32_t first, hipStream_t stream) {
     // statistics does not depend on how the roles are bound.
     const dpk::Table t = p->full.table(first && all_flat(grads, p->n) && all_flat(accs, p->n));
     if (t.npieces > 0) {
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, dpk::PieceSpan{0, t.npieces}, grads,
-                                                    accs, stream),
-                         "accumulate launch");
+        Reads rd;
+        rd.replicas(p, DP_ROLE_GRAD);
+        rd.replicas(p, DP_ROLE_ACC);
+        s = with_tables(p, rd, stream, "accumulate launch", [&] {
+            return dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, dpk::PieceSpan{0, t.npieces}, grads, accs,
+                                              stream);
+        });
         if (s != DP_OK) return s;
     }
     for (int32_t r = 0; r < p->n; ++r) p->micro[r] = first ? 1 : p->micro[r] + 1;
@@ -684,8 +877,12 @@ dp_status dp_accumulate_all_range(dp_plan* p, int32_t first, int64_t begin, int6
         bucket.log2s = p->full.log2s;
         const dpk::Table t = flat ? bucket.table(true) : p->full.table(false);
         const dpk::PieceSpan sp = flat ? dpk::PieceSpan{0, t.npieces} : dpk::PieceSpan{p0, p1};
-        s = check_launch(dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, sp, grads, accs, stream),
-                         "accumulate launch");
+        Reads rd;
+        rd.replicas(p, DP_ROLE_GRAD);
+        rd.replicas(p, DP_ROLE_ACC);
+        s = with_tables(p, rd, stream, "accumulate launch", [&] {
+            return dpk::launch_accumulate_all(p->gdt, first != 0, p->n, t, sp, grads, accs, stream);
+        });
         if (s != DP_OK) return s;
     }
     if (end > begin) {
@@ -746,9 +943,10 @@ static dp_status reduction_bucket(dp_plan* p, int src, int64_t begin, int64_t en
     }
     const dpk::Table t = p->full.table(false);  // statistics: table pieces, the slots of the whole reduction
     if (p1 > p0) {
-        s = check_launch(dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{p0, p1}, accs, grads, gb->ref(),
-                                            p->stats, stream),
-                         "reduce launch");
+        s = with_tables(p, reduction_reads(p, mode), stream, "reduce launch", [&] {
+            return dpk::launch_reduce(mode, p->gdt, p->n, t, dpk::PieceSpan{p0, p1}, accs, grads, gb->ref(), p->stats,
+                                      stream);
+        });
         if (s != DP_OK) return s;
     }
     if (end > begin) {
@@ -821,7 +1019,10 @@ dp_status dp_grad_stats(dp_plan* p, int32_t scan, double max_norm, hipStream_t s
         if (s != DP_OK) return s;
         const dpk::Table t = p->full.table(false);  // statistics: table pieces
         if (t.npieces > 0) {
-            s = check_launch(dpk::launch_stats(t, gb->ref(), p->stats, stream), "stats launch");
+            Reads rd;
+            rd.add(gbar_binding(p));
+            s = with_tables(p, rd, stream, "stats launch",
+                            [&] { return dpk::launch_stats(t, gb->ref(), p->stats, stream); });
             if (s != DP_OK) return s;
         }
         p->partials_count = t.npieces;
@@ -862,8 +1063,13 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
     const dpk::StateRefs sr = state_refs(p);
     const dpk::RoleRef pr = p->roles[DP_ROLE_PARAM][0].ref();
     const bool flat = all_flat(sr) && all_flat({gb->ref(), pr});
-    return check_launch(dpk::launch_adamw(p->pdt, t->table(flat), gb->ref(), sr, pr, p->state, a, stream),
-                        "adamw launch");
+    Reads rd;
+    rd.add(gbar_binding(p));
+    rd.state(p);
+    rd.add(&p->roles[DP_ROLE_PARAM][0]);
+    return with_tables(p, rd, stream, "adamw launch", [&] {
+        return dpk::launch_adamw(p->pdt, t->table(flat), gb->ref(), sr, pr, p->state, a, stream);
+    });
 }
 
 // The single pass's sources (every replica's last micro-step, plus its
@@ -899,11 +1105,17 @@ static dp_status single_pass_launch(dp_plan* p, const dp_adam_hparams* hp, bool 
                                     const dpk::Srcs& accs, int64_t p0, int64_t p1, hipStream_t stream) {
     if (p1 <= p0) return DP_OK;
     const dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
-    return check_launch(dpk::launch_reduce_adamw(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients,
-                                                 p->gdt, p->pdt, p->n, p->full.table(false), dpk::PieceSpan{p0, p1},
-                                                 accs, grads, state_refs(p), p->roles[DP_ROLE_PARAM][0].ref(),
-                                                 p->stats, p->state, a, stream),
-                        "reduce + adamw launch");
+    Reads rd;
+    rd.replicas(p, DP_ROLE_GRAD);
+    if (with_acc) rd.replicas(p, DP_ROLE_ACC);
+    rd.state(p);
+    rd.add(&p->roles[DP_ROLE_PARAM][0]);
+    return with_tables(p, rd, stream, "reduce + adamw launch", [&] {
+        return dpk::launch_reduce_adamw(with_acc ? dpk::ReduceMode::kAccPlusGrad : dpk::ReduceMode::kGradients, p->gdt,
+                                        p->pdt, p->n, p->full.table(false), dpk::PieceSpan{p0, p1}, accs, grads,
+                                        state_refs(p), p->roles[DP_ROLE_PARAM][0].ref(), p->stats, p->state, a,
+                                        stream);
+    });
 }
 
 // The end of a single pass: the statistics fold and the commit of the step
@@ -917,9 +1129,13 @@ static dp_status single_pass_commit(dp_plan* p, hipStream_t stream) {
     dp_status s = check_launch(dpk::launch_finalize(p->stats, p->full.npieces(false), p->fold, p->state, sc, stream),
                                "finalize launch");
     if (s != DP_OK) return s;
-    s = check_launch(dpk::launch_restore_param(p->pdt, p->full.table(all_flat(sr) && all_flat({pr})), sr, pr, p->state,
-                                               stream),
-                     "parameter restore launch");
+    Reads rd;
+    rd.state(p);
+    rd.add(&p->roles[DP_ROLE_PARAM][0]);
+    s = with_tables(p, rd, stream, "parameter restore launch", [&] {
+        return dpk::launch_restore_param(p->pdt, p->full.table(all_flat(sr) && all_flat({pr})), sr, pr, p->state,
+                                         stream);
+    });
     if (s != DP_OK) return s;
     std::fill(p->micro.begin(), p->micro.end(), 0);
     p->partials_valid = false;

@@ -125,6 +125,18 @@ hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int 
 hipError_t launch_restore_param(dp_dtype pdt, const Table& t, const StateRefs& s, RoleRef p, const DevState* st,
                                 hipStream_t stream);
 hipError_t launch_state_init(DevState* st, double scale, hipStream_t stream);
+
+// Copies of per-tensor pointer tables from pinned host memory (readable by
+// the device) into device tables, all of one launch's pending ones at once:
+// tables [0, count), T pointers each.
+constexpr int kMaxUploads = 2 * DP_MAX_REPLICAS + 8;
+struct TableUploads {
+    const void* const* src[kMaxUploads];
+    void** dst[kMaxUploads];
+    int32_t count;
+    int32_t T;
+};
+hipError_t launch_upload_tables(const TableUploads& u, hipStream_t stream);
 // The chunk table of one tensor [0, P) (chunks of 2^log2c elements) into
 // device memory `chunks`, and zeros in the statistics slots that no piece of
 // its npieces maps to (the fold adds them).

@@ -688,6 +688,14 @@ __global__ void __launch_bounds__(256) k_flat_table(dp_chunk* __restrict__ chunk
     }
 }
 
+// Workgroup b copies table b of the list: T pointers from pinned host memory
+// into its device table.
+__global__ void __launch_bounds__(256) k_upload_tables(TableUploads u) {
+    const void* const* __restrict__ src = u.src[blockIdx.x];
+    void** __restrict__ dst = u.dst[blockIdx.x];
+    for (int32_t i = static_cast<int32_t>(threadIdx.x); i < u.T; i += 256) dst[i] = const_cast<void*>(src[i]);
+}
+
 // ---- launch helpers ---------------------------------------------------------
 // Launches `launch(base, grid)` over pieces [p0, p1), one workgroup each, in
 // slices of at most kMaxBlocksPerLaunch (gridDim.y = ny); base is the piece
@@ -903,6 +911,12 @@ hipError_t launch_flat_table(dp_chunk* chunks, int64_t P, int log2c, StatsBuf sb
     const int64_t work = nchunks > 8 ? nchunks : 8;
     hipLaunchKernelGGL(k_flat_table, dim3(static_cast<unsigned>((work + 255) / 256)), dim3(256), 0, s, chunks, P,
                        log2c, nchunks, sb, npieces);
+    return hipGetLastError();
+}
+
+hipError_t launch_upload_tables(const TableUploads& u, hipStream_t s) {
+    if (u.count <= 0 || u.count > kMaxUploads || u.T <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_upload_tables, dim3(static_cast<unsigned>(u.count)), dim3(256), 0, s, u);
     return hipGetLastError();
 }
 

@@ -14,13 +14,46 @@ namespace dpapi {
 
 constexpr int kNumRoles = 7;
 
+// Per-tensor pointer tables of one role live in a ring of kRingSlots device
+// tables.  A rebinding fills the next slot's pinned staging copy on the host
+// and returns; the next launch that reads the role uploads it on that
+// launch's own stream, ahead of itself (one small kernel copies every table
+// the launch finds pending), and launches on other streams wait for that
+// upload.  Launches still reading an earlier slot are undisturbed.
+// A slot is written again only kRingSlots rebindings later, after the
+// launches that read it (events recorded behind each) have finished.
+constexpr int kRingSlots = 4;
+
+// Events shared by the pointer-table slots: one is recorded behind each
+// launch that reads per-tensor tables and one behind each upload of tables,
+// and every slot involved holds a reference, so a launch adds at most two
+// event records to its stream however many tables it reads.  An event
+// returns to the free list when its last reference goes.
+struct EventPool {
+    std::vector<hipEvent_t> ev;
+    std::vector<int> refs;
+    std::vector<int> free_list;
+};
+
 // Where one role's memory is: one flat buffer, or one pointer per tensor
-// (kept on the host and mirrored in a device table for the kernels).
+// (kept on the host and mirrored in the current slot of the device ring).
 struct Binding {
     void* flat = nullptr;
-    std::vector<void*> tensors;
-    void** dev_table = nullptr;
+    std::vector<void*> tensors;  // host copy of the per-tensor pointers
+    void** dev_table = nullptr;  // device table of the current slot; null for a flat binding
     bool bound = false;
+
+    void** ring_dev = nullptr;   // kRingSlots device tables of T pointers (first per-tensor binding)
+    void** ring_host = nullptr;  // their pinned staging copies
+    void** ring_host_dev = nullptr;  // the staging copies' device-side address
+    int slot = -1;               // current slot
+    bool pending = false;        // the current slot's staging copy is not on the device yet
+    // events of the plan's pool (EventPool indices, -1: none) that a slot
+    // holds: behind its upload, and per stream behind the last launch there
+    // that read it
+    int uploaded[kRingSlots] = {-1, -1, -1, -1};
+    hipStream_t upload_stream[kRingSlots] = {};
+    std::vector<std::pair<hipStream_t, int>> uses[kRingSlots];
 
     dpk::RoleRef ref() const { return dpk::RoleRef{flat, dev_table}; }
 };
@@ -55,6 +88,7 @@ struct dp_plan {
     dp_dtype gdt = DP_BF16, pdt = DP_BF16;
 
     dpapi::Binding roles[dpapi::kNumRoles][DP_MAX_REPLICAS];
+    dpapi::EventPool events;  // of the per-tensor pointer-table rings
 
     // device resources (allocated by dp_state_init / prepare / bind_tensors)
     int device = -1;

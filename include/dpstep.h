@@ -195,15 +195,24 @@ dp_status dp_plan_chunks(const dp_plan* plan, int64_t begin, int64_t end, int64_
 
 /* Binds one contiguous device buffer to a role: tensor i starts at element
  * prefix[i] of it.  replica selects the GRAD / ACC buffer, or the bank (0, 1)
- * of MASTER / EXP_AVG / EXP_AVG_SQ; 0 for PARAM and GBAR.  Host work only;
- * rebinding is cheap and may happen between any two calls. */
+ * of MASTER / EXP_AVG / EXP_AVG_SQ; 0 for PARAM and GBAR.  Host work only
+ * (a role's pointer-table ring, if it has one, is kept for later per-tensor
+ * bindings); rebinding is cheap and may happen between any two calls. */
 dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* device_base);
 
 /* Binds one device pointer per tensor (host array ptrs[num_tensors]).  The
- * pointer table is copied to the device: the first binding of a role
- * allocates its table; a rebinding rewrites it in place after synchronising
- * the device, so work already launched with the old pointers, on any stream,
- * is finished first.  If the copy fails the role is left unbound. */
+ * kernels read the pointers from a device table.  Each role keeps a ring of
+ * four such tables; the first per-tensor binding of a role allocates the ring
+ * (device memory and pinned host staging), which lasts until
+ * dp_plan_destroy.  A rebinding copies ptrs into the next slot's staging
+ * memory and returns without synchronising: the next compute call that
+ * reads the role uploads the table on its own stream before its launch,
+ * and calls on other streams wait for that upload.  Work already launched
+ * with an earlier table keeps reading it undisturbed.  A slot is rewritten
+ * only four rebindings later, after the launches that read it have finished
+ * (the rebinding waits for them then, if they have not).  Rebinding the
+ * pointers already bound does nothing.  Suited to rebinding per micro-step,
+ * for example gradients in per-tensor buffers that change every step. */
 dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
 
 /* Builds and uploads the chunk table of [begin, end) so later dp_adam_step
@@ -218,7 +227,19 @@ dp_status dp_plan_prepare_range(dp_plan* plan, int64_t begin, int64_t end);
  * again.  Nothing else of the plan changes. */
 dp_status dp_plan_drop_ranges(dp_plan* plan);
 
-/* Allocates the device state and statistics scratch on the current device
+/* The per-run scalar state of the step: the applied-step count t and the
+ * bias-correction powers of Adam, and the loss scale with its growth
+ * tracker.  The pages count loss scaling among the training state a
+ * checkpoint must hold, beside the optimizer's ("Distributed Training: Split
+ * along the Four Axes of Data, Tensor, Pipeline, and State",
+ * ai-knowledge-map.com: checkpoint-contents paragraph), and ask that it stay
+ * aligned with the baseline when runs are compared (same page, evaluation
+ * paragraph on training semantics).  The scaler policies themselves
+ * (dp_scaler_mode: skip on a non-finite gradient, back off, grow after a
+ * run of clean steps) are not on the pages; they follow the workloads this
+ * library is built for, which name a static and a dynamic loss scale.
+ *
+ * Allocates the device state and statistics scratch on the current device
  * (first call), and sets t = 0, beta powers = 1, scale = init_scale (1 with
  * DP_SCALER_NONE), growth tracker 0, asynchronously on stream. */
 dp_status dp_state_init(dp_plan* plan, const dp_state_cfg* cfg, hipStream_t stream);
@@ -305,7 +326,19 @@ dp_status dp_reduce_replicas_range(dp_plan* plan, dp_role src, int64_t begin, in
  * DP_ERR_STATE) or DP_ROLE_GRAD (n low-precision partials, a = 1). */
 dp_status dp_reduce_replicas(dp_plan* plan, dp_role src, hipStream_t stream);
 
-/* Global statistics and per-step scalars.  scan != 0 first reads GBAR to
+/* Global statistics and per-step scalars of g_bar: its sum of squares and
+ * whether it holds an inf or NaN, then the step's scalars.  The pages ask
+ * that the reduction's numerics be aligned between runs, naming loss
+ * scaling and reduction precision together ("Distributed Training ...":
+ * evaluation paragraph on training semantics, and the reduction-order
+ * paragraph: the summation order changes the bits), and count loss scaling
+ * as state (checkpoint-contents paragraph).  The sum of squares is kept in
+ * binary64 in a fixed order.  Global-norm clipping (max_norm) is not on the
+ * pages: it comes from the workloads this library is built for, which clip
+ * at 1.0; the norm is the unscaled one over the whole plan, so a shard's
+ * update equals the unsharded one (same page, ZeRO paragraph).
+ *
+ * scan != 0 first reads GBAR to
  * write the per-chunk statistics; scan == 0 uses those written by
  * dp_reduce_replicas or dp_accumulate(emit_stats) (DP_ERR_STATE if there are
  * none).  Then, on the device: norm = sqrt(sum g_bar^2) / scale; if any entry

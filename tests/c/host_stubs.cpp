@@ -34,5 +34,6 @@ hipError_t launch_restore_param(dp_dtype, const Table&, const StateRefs&, RoleRe
     return hipErrorNotSupported;
 }
 hipError_t launch_state_init(DevState*, double, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_upload_tables(const TableUploads&, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace dpk

@@ -1,8 +1,12 @@
 """The plan's life cycle on the GPU, through the C ABI: a failed allocation of
 the state leaves nothing behind and the plan usable for error reporting;
 per-tensor pointer tables rebound between launches on a non-default stream
-never reach a kernel that was launched with the old ones; and cached range
-tables can be dropped when the shard partition changes during a run."""
+never reach a kernel that was launched with the old ones, a rebinding does
+not wait for the device, and launches on two streams read a rebound table
+after its upload; and cached range tables can be dropped when the shard
+partition changes during a run."""
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -130,3 +134,91 @@ def test_shard_ranges_change_over_a_run():
     ref = oracle_run(w, 4)
     assert_scalars_match(state, ref.scalars[-1], where="changing shards")
     assert_state_close(got, ref.state[(0, P)], ulp_bound(w), where="changing shards")
+
+
+def _busy(stream, products: int = 60):
+    """Queues binary32 matrix products of 8192 x 8192 (about 7 ms each) on
+    `stream` and returns an event recorded behind them."""
+    with torch.cuda.stream(stream):
+        a = torch.randn(8192, 8192, device="cuda") * (1.0 / 8192)
+        for _ in range(products):
+            a = a @ a
+        ev = torch.cuda.Event()
+        ev.record(stream)
+    return ev, a
+
+
+def test_rebinding_does_not_wait_for_the_gpu():
+    """A per-tensor rebinding returns while earlier work still runs on the
+    device, and the next launch reads the new pointers."""
+    numel = (4099, 70001, 256)
+    P, T = sum(numel), len(numel)
+    off = np.concatenate([[0], np.cumsum(numel)])
+    stream = torch.cuda.Stream()
+    s = stream.cuda_stream
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    g = [(torch.randn(P, generator=gen, device="cuda") * 1e-3).to(torch.bfloat16) for _ in range(2)]
+    acc = torch.zeros(P, dtype=torch.float32, device="cuda")
+
+    def per_tensor(buf):
+        return [buf[int(off[t]):int(off[t + 1])] for t in range(T)]
+
+    plan = dp.Plan(numel, 1, "bf16", "bf16")
+    try:
+        plan.bind("acc", acc, 0)
+        plan.bind_tensors("grad", per_tensor(g[0]), 0)  # the first binding allocates the ring
+        plan.accumulate_all(first=True, stream=s)
+        torch.cuda.synchronize()
+        ev, keep = _busy(stream)
+        waits = []
+        for i, k in enumerate((1, 0, 1)):  # three rebindings, each followed by a launch behind the busy work
+            t = time.perf_counter()
+            plan.bind_tensors("grad", per_tensor(g[k]), 0)
+            waits.append(time.perf_counter() - t)
+            plan.accumulate_all(first=(i == 0), stream=s)
+        still_busy = not ev.query()
+        torch.cuda.synchronize()
+        log(f"rebinding took {[f'{x * 1e3:.3f} ms' for x in waits]}; GPU still busy after them: {still_busy}")
+        assert still_busy, "the busy work finished before the rebindings: the check says nothing"
+        assert max(waits) < 0.05
+        # g[1] as the first micro-step, then g[0] and g[1] added, in binary32
+        want = g[1].float() + g[0].float() + g[1].float()
+        assert torch.equal(acc.view(torch.int32), want.view(torch.int32))
+        del keep
+    finally:
+        plan.close()
+
+
+def test_rebound_tables_read_from_two_streams():
+    """Micro-steps in buckets, the even buckets on one stream and the odd on
+    another, with the GRAD table rebound before every micro-step: the first
+    launch after a rebinding uploads the table on its stream and the other
+    stream waits for that upload.  Six rebindings wrap the ring of four slots.
+    The accumulators equal the binary32 sums bit for bit."""
+    numel = (3000, 17, 70001, 4096, 65536 + 256)
+    P, T = sum(numel), len(numel)
+    off = np.concatenate([[0], np.cumsum(numel)])
+    micro = 6
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    g = [(torch.randn(P, generator=gen, device="cuda") * 1e-3).to(torch.bfloat16) for _ in range(micro)]
+    acc = torch.zeros(P, dtype=torch.float32, device="cuda")
+    buckets = driver.backward_buckets(numel, 16 << 10)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    plan = dp.Plan(numel, 1, "bf16", "bf16")
+    try:
+        plan.bind("acc", acc, 0)
+        for k in range(micro):
+            plan.bind_tensors("grad", [g[k][int(off[t]):int(off[t + 1])] for t in range(T)], 0)
+            for i, (lo, hi) in enumerate(buckets):
+                plan.accumulate_all_range(k == 0, lo, hi, stream=streams[i % 2].cuda_stream)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    want = g[0].float()
+    for k in range(1, micro):
+        want = want + g[k].float()
+    log(f"{len(buckets)} buckets on two streams, {micro} rebound micro-steps")
+    assert torch.equal(acc.view(torch.int32), want.view(torch.int32))
