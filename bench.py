@@ -22,6 +22,7 @@ import os
 import statistics
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -50,7 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
     ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
-                    help="bind the state as flat buffers, or through per-tensor pointer tables (same memory)")
+                    help="bind the state as flat buffers, or through per-tensor pointer tables (same memory); "
+                         "with tensors the gradients are also bound per tensor, rebound before every micro-step")
     ap.add_argument("--update", choices=("auto", "two-pass", "single-pass"), default="auto",
                     help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
                          "update in one read of the state (runs without clipping); auto: single-pass when the "
@@ -85,6 +87,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run a plain device copy of BYTES bytes (3 times), as the reference kernel of the "
                          "FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print a table of the per-dispatch averages of every counter in these rocprofv3 --pmc "
+                         "counter_collection.csv files, per kernel kind, with the derived latencies and stall "
+                         "shares, then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/traffic.json, then exit")
@@ -141,6 +147,67 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, calib_byte
                      "bytes_per_launch": fk * 1024.0 * f_fac + wk * 1024.0 * w_fac,
                      "kernel_source_sha": kernel_source_hash()}
     return {workload: out, "calibration": {"copy_bytes": calib_bytes, "fetch_kib": f_kib, "write_kib": w_kib}}
+
+
+# kernel kinds of a counter summary: the library's calls and the bandwidth
+# references of measure_ceilings
+PMC_KINDS = dict(KERNEL_NAMES, copy_probe=r"stream_copy", read_probe=r"stream_read")
+
+
+def summarize_pmc(paths) -> str:
+    """Per kernel kind, the average over its dispatches of every counter in
+    the files (rocprofv3 --pmc counter_collection.csv), and what follows from
+    them: the L2's average read and write latency to memory (cycles per
+    request in flight), the share of L2 cycles its requests spent stalled for
+    want of DRAM credits, the share of 32-byte read and 64-byte write
+    requests, and the bytes a dispatch moved per microsecond under counters."""
+    import csv
+    import re
+
+    vals, durs = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            kind = next((k for k, rx in PMC_KINDS.items() if re.search(rx, r.get("Kernel_Name", ""))), None)
+            if kind is None:
+                continue
+            vals.setdefault(kind, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                key = (path, r["Dispatch_Id"])
+                durs.setdefault(kind, {})[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    lines = []
+    for kind in PMC_KINDS:
+        if kind not in vals:
+            continue
+        avg = {k: sum(v) / len(v) for k, v in vals[kind].items()}
+        d = list(durs.get(kind, {}).values())
+        lines.append(f"### {kind}: {max(len(v) for v in vals[kind].values())} dispatches"
+                     + (f", {sum(d) / len(d):.1f} us average under counters" if d else ""))
+        lines.append("| counter | average per dispatch |")
+        lines.append("|---|---:|")
+        for k in sorted(avg):
+            lines.append(f"| {k} | {avg[k]:.6g} |")
+
+        def ratio(a, b):
+            return avg[a] / avg[b] if a in avg and b in avg and avg[b] else None
+
+        derived = {
+            "read latency (L2 cycles per request)": ratio("TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum"),
+            "write latency (L2 cycles per request)": ratio("TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_WRREQ_sum"),
+            "read DRAM-credit stall share of L2 cycles": ratio("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_CYCLE_sum"),
+            "write DRAM-credit stall share of L2 cycles": ratio("TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_CYCLE_sum"),
+            "write stall share of L2 cycles": ratio("TCC_EA0_WRREQ_STALL_sum", "TCC_CYCLE_sum"),
+            "32-byte share of read requests": ratio("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_sum"),
+            "64-byte share of write requests": ratio("TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_sum"),
+            "L2 hit share": (avg["TCC_HIT_sum"] / (avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"])
+                             if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg and
+                             avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"] else None),
+            "vector memory latency (cycles per instruction in flight)": ratio("SQ_INST_LEVEL_VMEM", "SQ_INSTS_VMEM"),
+        }
+        for k, v in derived.items():
+            if v is not None:
+                lines.append(f"| *{k}* | {v:.4g} |")
+        lines.append("")
+    return "\n".join(lines)
 
 
 def kernel_source_hash() -> str:
@@ -265,7 +332,7 @@ def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
     constant fill 2-4% faster than the random values the workloads carry."""
     import torch
 
-    import synth
+    import benchprobe
 
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
@@ -284,14 +351,83 @@ def measure_ceilings(nbytes: int = 4 << 30, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3
 
-    t_copy = timed(lambda: synth.stream_probe("copy", src.data_ptr(), dst.data_ptr(), nbytes, s))
-    t_read = timed(lambda: synth.stream_probe("read", src.data_ptr(), 0, nbytes, s))
+    t_copy = timed(lambda: benchprobe.stream("copy", src.data_ptr(), dst.data_ptr(), nbytes, s))
+    t_read = timed(lambda: benchprobe.stream("read", src.data_ptr(), 0, nbytes, s))
     t_rt = timed(lambda: dst.copy_(src))
     del src, dst
     torch.cuda.empty_cache()
     return {"copy_gbps": 2 * nbytes / t_copy / 1e9, "read_gbps": nbytes / t_read / 1e9,
             "runtime_copy_gbps": 2 * nbytes / t_rt / 1e9, "bytes": nbytes,
             "what": "one-shot wave64 copy and read (16 B per lane, nontemporal) of random bytes; runtime copy = torch copy_"}
+
+
+def mix_spec(w, kind: str) -> Optional[dict]:
+    """The streams one launch of `kind` reads and writes per element, as a
+    benchprobe mix: 16-bit and binary32 streams read, binary32 and 16-bit
+    streams written, and whether the first binary32 stream is updated in
+    place."""
+    n = w.n
+    earlier = not w.partials and w.a >= 2  # the last micro-step adds to accumulators
+    if kind == "accumulate":
+        return dict(r16=1, r32=1, w32=1, w16=0, rmw=True)
+    if kind == "accumulate_reduce":
+        return dict(r16=n, r32=n if earlier else 0, w32=1, w16=0, rmw=False)
+    if kind == "adamw":
+        return dict(r16=0, r32=4, w32=3, w16=1, rmw=False)
+    if kind == "reduce_adamw" and (not earlier or n <= 13):
+        return dict(r16=n, r32=3 + (n if earlier else 0), w32=3, w16=1, rmw=False)
+    return None
+
+
+def measure_mix(w, kind: str, reps: int = 10, max_elems: int = 1 << 29) -> Optional[dict]:
+    """The bandwidth the stream mix of `kind` reaches on this GPU: the same
+    arrays, access shape and hints as the library's kernel with no arithmetic
+    beyond a sum (benchprobe.mix), over min(P, 2^29) elements of random data
+    in the workload's value ranges (16-bit streams: bf16 of N(0, 1e-4);
+    binary32 streams: N(0, 0.02)); the better of two shapes, with and without
+    the staggered start of the library's table-driven kernels."""
+    import torch
+
+    import benchprobe
+
+    spec = mix_spec(w, kind)
+    if spec is None:
+        return None
+    N = min(w.P, max_elems) // 256 * 256
+    if N == 0:
+        return None
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1)
+    r16 = [(torch.randn(N, generator=gen, device="cuda") * 1e-4).to(torch.bfloat16) for _ in range(spec["r16"])]
+    r32 = [torch.randn(N, generator=gen, device="cuda") * 0.02 for _ in range(spec["r32"])]
+    w32 = ([r32[0]] if spec["rmw"] else []) + [torch.empty(N, device="cuda")
+                                               for _ in range(spec["w32"] - (1 if spec["rmw"] else 0))]
+    w16 = [torch.empty(N, dtype=torch.int16, device="cuda") for _ in range(spec["w16"])]
+    stag = torch.zeros(N // 16384 + 1, dtype=torch.int64, device="cuda")
+    addr = lambda ts: [t.data_ptr() for t in ts]  # noqa: E731
+    st = torch.cuda.current_stream()
+    per = 2 * spec["r16"] + 4 * spec["r32"] + 4 * spec["w32"] + 2 * spec["w16"]
+    shapes = {}
+    for shape, sp in (("plain", 0), ("staggered", stag.data_ptr())):
+        def once():
+            benchprobe.mix(addr(r16), addr(r32), addr(w32), addr(w16), N, st.cuda_stream, rmw=spec["rmw"],
+                           stagger=sp)
+
+        once()
+        once()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            once()
+        e1.record(st)
+        torch.cuda.synchronize()
+        shapes[shape] = per * N / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    gbps = max(shapes.values())
+    del r16, r32, w32, w16, stag
+    torch.cuda.empty_cache()
+    return {"mix": {k: v for k, v in spec.items()}, "bytes_per_elem": per, "elements": N, "gbps_by_shape": shapes,
+            "gbps": gbps, "frac": gbps / PEAK_HBM_GBPS}
 
 
 def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: str = "flat", single: bool = False,
@@ -358,6 +494,17 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     torch.cuda.synchronize()
 
     plan = d.plan
+    off_bytes = [2 * int(x) for x in w.offsets[:-1]]
+
+    def bind_grad(r, a):
+        # flat: one base per replica; tensors: one pointer per tensor, a new
+        # table before every micro-step as a framework with per-tensor
+        # gradient buffers would bind them
+        if bind == "tensors":
+            plan.bind_tensors("grad", [a + o for o in off_bytes], r)
+        else:
+            dp_plan_bind_flat(plan.handle, DP_ROLE_GRAD, r, a)
+
     events = {}
     sink = [events]  # where timed() records: the timed run's events, or one logged step's
 
@@ -373,15 +520,14 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
             fn()
 
     def one_step(rec: bool):
-        h = plan.handle
         last = 1 if w.partials else w.a
         for k in range(1, last):
             for r in range(w.n):
-                dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, k)])
+                bind_grad(r, addr[(r, k)])
             timed("accumulate_first" if k == 1 else "accumulate",
                   lambda k=k: plan.accumulate_all(first=(k == 1), stream=stream), rec)
         for r in range(w.n):
-            dp_plan_bind_flat(h, DP_ROLE_GRAD, r, addr[(r, last)])
+            bind_grad(r, addr[(r, last)])
         if single:  # one call: the single-pass kernel, the statistics fold and the (idle) parameter restore
             timed("reduce_adamw", lambda: plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
             return
@@ -474,6 +620,7 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
     bucketed and overlapped too."""
     import torch
 
+    import benchprobe
     import synth
     from gradient_reduce_adam_amd import driver
 
@@ -489,7 +636,7 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
     addrs = [t.data_ptr() for t in slots]
 
     def produce(step, k, lo, hi, stream):
-        synth.backward_bucket(wi, step, k, lo, hi, addrs, d.scale, stream, tokens)
+        benchprobe.backward_bucket(wi, step, k, lo, hi, addrs, d.scale, stream, tokens)
 
     def timed(fn, reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -690,7 +837,10 @@ def zero3_single_pass(steps: int, warmup: int, placements: int) -> dict:
                      "skipped_step_ms": per_kind.get("skipped_step_ms")})
     fr = sorted(r["frac"] for r in runs)
     med = statistics.median(r["ms_per_step"] for r in runs)
-    return {"workload": w.name, "params": w.P, "update": "single-pass", "steps": steps,
+    ceiling = measure_mix(w, "reduce_adamw")
+    if ceiling:
+        ceiling["library_of_ceiling_median"] = statistics.median(r["reduce_adamw_gbps"] for r in runs) / ceiling["gbps"]
+    return {"workload": w.name, "mix_ceiling": ceiling, "params": w.P, "update": "single-pass", "steps": steps,
             "bytes_per_param_step": sum(per_param.values()),
             "ms_per_step_median": med, "params_per_s_median": w.P / (med * 1e-3),
             "hbm_gbps_median": sum(per_param.values()) * w.P / (med * 1e-3) / 1e9,
@@ -711,6 +861,9 @@ def main():
         sys.exit(2)
     from synth import workloads
 
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.summarize_counters:
         res = summarize_counters(*args.summarize_counters, args.workload, args.copy_calibration)
         old = {}
@@ -752,7 +905,16 @@ def main():
         ent = t.get(w.name, {}).get(dom)
         if ent and ent.get("kernel_source_sha") == kernel_source_hash():
             traffic = ent["bytes_per_launch"]
-    progress("measured ceilings (copy and read of random bytes)")
+    progress("measured ceilings (copy and read of random bytes, and the stream mixes of the main kernels)")
+    mix = {}
+    if args.state == "hbm":
+        for kind in [k for k in per_param if k in per_kind]:
+            m = measure_mix(w, kind)
+            if m:
+                lib_gbps = launch_bytes(w, kind, single) / (per_kind[kind]["avg_ms"] * 1e-3) / 1e9
+                m["library_gbps"] = lib_gbps
+                m["library_of_ceiling"] = lib_gbps / m["gbps"]
+                mix[kind] = m
 
     line = {
         "metric": "params updated/sec and achieved HBM GB/s (% of peak) per full DP step",
@@ -793,7 +955,7 @@ def main():
         "step_ms_median": statistics.median(step_ms) if step_ms else None,
         "step_ms_min": step_ms[0] if step_ms else None,
         "device": device_info(),
-        "measured_ceilings": measure_ceilings(),
+        "measured_ceilings": dict(measure_ceilings(), stream_mixes=mix),
         "cpu_baseline": None,
     }
     if args.state == "host":

@@ -130,11 +130,6 @@ def _gpu_lib():
         lib.synth_normal_device_multi.argtypes = [ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_void_p),
                                                   ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                                   ctypes.c_int, ctypes.c_void_p]
-        lib.synth_busy_device.restype = ctypes.c_int
-        lib.synth_busy_device.argtypes = [ctypes.c_double, ctypes.c_void_p]
-        lib.synth_stream_probe.restype = ctypes.c_int
-        lib.synth_stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                           ctypes.c_void_p]
         _gpu = lib
     return _gpu
 
@@ -234,28 +229,6 @@ def master_device(w, out_ptr: int, stream: int, lo: int = 0, hi: Optional[int] =
     device_normal(master_key(w), lo, hi - lo, scale_constant(w.master_sigma), "f32", out_ptr, stream)
 
 
-def stream_probe(kind: str, src_ptr: int, dst_ptr: int, nbytes: int, stream: int) -> None:
-    """One pass of a bandwidth reference kernel (benchmark infrastructure):
-    kind "copy" copies nbytes from src to dst, "read" reads nbytes of src."""
-    rc = _gpu_lib().synth_stream_probe({"copy": 0, "read": 1}[kind], ctypes.c_void_p(src_ptr),
-                                       ctypes.c_void_p(dst_ptr), int(nbytes), ctypes.c_void_p(stream))
-    if rc != 0:
-        raise RuntimeError(f"synth_stream_probe failed with code {rc}")
-
-
-def busy_device(flops: float, stream: int) -> None:
-    """Matrix-core work of about `flops` operations on `stream`, touching no
-    memory: the compute part of a synthetic backward pass."""
-    rc = _gpu_lib().synth_busy_device(float(flops), ctypes.c_void_p(stream))
-    if rc != 0:
-        raise RuntimeError(f"synth_busy_device failed with code {rc}")
-
-
-# Backward-pass compute per parameter and token: about twice the forward's
-# 2 flops per parameter and token.
-BACKWARD_FLOPS_PER_PARAM_TOKEN = 4.0
-
-
 def grads_device_replicas(w, step: int, micro: int, slots, loss_scale: float, stream: int, lo: int = 0,
                           hi: Optional[int] = None) -> None:
     """``grad_device`` for every replica at once (one launch per piece of
@@ -273,17 +246,6 @@ def grads_device_replicas(w, step: int, micro: int, slots, loss_scale: float, st
     for r in range(n):
         for idx, val in _injected(w, step, r, micro, lo, hi):
             _poke_u16(slots[r] + 2 * idx, _lp_bits(val, w.grad_dtype), stream)
-
-
-def backward_bucket(w, step: int, micro: int, lo: int, hi: int, slots, loss_scale: float, stream: int,
-                    tokens: int) -> None:
-    """A synthetic backward pass over the parameters [lo, hi): the matrix-core
-    compute of one replica's backward for those parameters at `tokens` tokens
-    per micro-batch, then every replica's gradients of [lo, hi) written into
-    its slot (slots[r]: device address of replica r's gradient buffer, which
-    holds the whole flat space)."""
-    busy_device(BACKWARD_FLOPS_PER_PARAM_TOKEN * (hi - lo) * tokens, stream)
-    grads_device_replicas(w, step, micro, slots, loss_scale, stream, lo, hi)
 
 
 def _poke_u16(ptr: int, bits: int, stream: int) -> None:

@@ -101,78 +101,9 @@ __global__ void poke_u16(uint16_t* p, uint32_t bits) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = static_cast<uint16_t>(bits);
 }
 
-// Stand-in for the compute of a backward pass: every wave chains `iters`
-// bf16 matrix-core products of 32x32x8 (16384 flops each) on register tiles,
-// reading and writing no memory.  The sum of the result feeds a comparison
-// that never holds, so the products are not removed.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kBusyThreads = 256;
-constexpr unsigned kBusyBlocks = 1024;
-constexpr double kFlopsPerProduct = 2.0 * 32 * 32 * 8;
-
-__global__ void __launch_bounds__(kBusyThreads) busy_mfma(int64_t iters, float* sink) {
-    const short v = static_cast<short>(threadIdx.x);
-    const s16x4 a = {v, 1, 2, 3};
-    const s16x4 b = {3, 2, 1, v};
-    f32x16 acc = {};
-    for (int64_t i = 0; i < iters; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, acc, 0, 0, 0);
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s += acc[e];
-    if (s == -1.0f && sink != nullptr) sink[0] = s;
-}
-
-// Bandwidth references for the benchmark, shaped like the library's streaming
-// kernels: one-shot wave64 workgroups, 16-byte accesses per lane, nontemporal
-// hints.  The copy reads and writes one KiB per wave; the read takes four KiB
-// per wave (a single KiB leaves it bound by how fast waves launch), sums them
-// and stores only when the sum equals a value the caller's data never holds.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-#define SYNTH_GLOBAL __attribute__((address_space(1)))
-
-__global__ void __launch_bounds__(64) stream_copy(const f32x4* src, f32x4* dst, int64_t nvec) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
-    if (i < nvec)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(((const SYNTH_GLOBAL f32x4*)src) + i),
-                                    ((SYNTH_GLOBAL f32x4*)dst) + i);
-}
-
-__global__ void __launch_bounds__(64) stream_read(const f32x4* src, int64_t nvec, float* sink) {
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t i = base + 64 * j;
-        if (i < nvec) {
-            const f32x4 v = __builtin_nontemporal_load(((const SYNTH_GLOBAL f32x4*)src) + i);
-            s += (v.x + v.y) + (v.z + v.w);
-        }
-    }
-    if (s == -1.0f && sink != nullptr) sink[0] = s;
-}
-
 }  // namespace
 
 extern "C" {
-
-// One pass of a bandwidth reference over `bytes` bytes (a multiple of 1024):
-// kind 0 copies src to dst, kind 1 reads src (dst unused).  Returns 0, -1 on a
-// bad argument, or the HIP error code.
-int synth_stream_probe(int kind, const void* src, void* dst, int64_t bytes, hipStream_t stream) {
-    if (src == nullptr || bytes <= 0 || bytes % 1024 != 0 || (kind == 0 && dst == nullptr) || kind < 0 || kind > 1)
-        return -1;
-    const int64_t nvec = bytes / 16;
-    const int64_t blocks = kind == 0 ? nvec / 64 : (nvec + 255) / 256;
-    if (blocks > (int64_t{1} << 31) - 1) return -1;
-    const dim3 grid(static_cast<unsigned>(blocks));
-    if (kind == 0)
-        hipLaunchKernelGGL(stream_copy, grid, dim3(64), 0, stream, static_cast<const f32x4*>(src),
-                           static_cast<f32x4*>(dst), nvec);
-    else
-        hipLaunchKernelGGL(stream_read, grid, dim3(64), 0, stream, static_cast<const f32x4*>(src), nvec, nullptr);
-    return static_cast<int>(hipGetLastError());
-}
 
 // Overwrites one 16-bit element (used to inject a non-finite gradient value).
 int synth_poke_u16(void* p, uint32_t bits, hipStream_t stream) {
@@ -219,19 +150,6 @@ int synth_normal_device_multi(const uint64_t* keys, const void* const* outs, int
         case 1: hipLaunchKernelGGL(gen_normal_multi<1>, grid, block, 0, stream, m, start, count, c); break;
         default: hipLaunchKernelGGL(gen_normal_multi<2>, grid, block, 0, stream, m, start, count, c); break;
     }
-    return static_cast<int>(hipGetLastError());
-}
-
-// Occupies the matrix cores with about `flops` floating-point operations
-// (bf16 products, rounded up to whole products per wave) on `stream`: the
-// compute of a synthetic backward pass.  Returns 0, -1 on a bad argument, or
-// the HIP error code.
-int synth_busy_device(double flops, hipStream_t stream) {
-    if (!(flops >= 0.0)) return -1;
-    const double waves = static_cast<double>(kBusyBlocks) * (kBusyThreads / 64);
-    const int64_t iters = static_cast<int64_t>(flops / (waves * kFlopsPerProduct) + 0.999999);
-    if (iters == 0) return 0;
-    hipLaunchKernelGGL(busy_mfma, dim3(kBusyBlocks), dim3(kBusyThreads), 0, stream, iters, nullptr);
     return static_cast<int>(hipGetLastError());
 }
 
