@@ -746,7 +746,7 @@ def device_info() -> dict:
     return info
 
 
-def cpu_share() -> dict:
+def cpu_share(cgroup_cpu_max: str = "/sys/fs/cgroup/cpu.max") -> dict:
     """The host threads this process may use: the cores of its affinity mask,
     capped by a cgroup CPU quota and by OMP_NUM_THREADS where either is set
     (a machine shared between GPUs gives each GPU's jobs a share of its
@@ -754,7 +754,7 @@ def cpu_share() -> dict:
     affinity = len(os.sched_getaffinity(0))
     quota = None
     try:
-        with open("/sys/fs/cgroup/cpu.max") as f:
+        with open(cgroup_cpu_max) as f:
             q, period = f.read().split()[:2]
         if q != "max":
             quota = max(1, int(math.ceil(int(q) / int(period))))
