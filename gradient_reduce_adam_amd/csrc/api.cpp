@@ -135,25 +135,12 @@ dp_status ensure_full(dp_plan* p) {
     return upload_table(p, 0, p->P, &p->full, &p->full_host);
 }
 
-dp_status range_table(dp_plan* p, int64_t begin, int64_t end, const DeviceTable** out) {
-    if (begin == 0 && end == p->P) {
-        dp_status s = ensure_full(p);
-        *out = &p->full;
-        return s;
-    }
-    dp_status s = ensure_device(p);
-    if (s != DP_OK) return s;
-    for (const DeviceTable& t : p->ranges)
-        if (t.begin == begin && t.end == end) {
-            *out = &t;
-            return DP_OK;
-        }
-    DeviceTable t;
-    s = upload_table(p, begin, end, &t);
-    if (s != DP_OK) return s;
-    p->ranges.push_back(t);
-    *out = &p->ranges.back();
-    return DP_OK;
+// The piece of the [0, P) table that holds flat element x (0 <= x < P).
+int64_t piece_holding(const dp_plan* p, int64_t x) {
+    const auto& ch = p->full_host;
+    const auto it = std::upper_bound(ch.begin(), ch.end(), x, [](int64_t v, const dp_chunk& c) { return v < c.flat; });
+    const int64_t c = static_cast<int64_t>(it - ch.begin()) - 1;
+    return (c << p->full.log2s) + (x - ch[static_cast<size_t>(c)].flat) / dpk::kPiece;
 }
 
 bool role_ok(dp_role r) { return r >= DP_ROLE_PARAM && r <= DP_ROLE_GBAR; }
@@ -512,8 +499,6 @@ dp_status dp_plan_destroy(dp_plan* p) {
             for (auto& b : row) free_ring(b);
         for (hipEvent_t ev : p->events.ev) (void)hipEventDestroy(ev);
         if (p->full.dev) (void)hipFree(p->full.dev);
-        for (auto& t : p->ranges)
-            if (t.dev) (void)hipFree(t.dev);
         if (p->state) (void)hipFree(p->state);
         if (p->stats.sumsq) (void)hipFree(p->stats.sumsq);
         if (p->stats.bad) (void)hipFree(p->stats.bad);
@@ -638,8 +623,7 @@ dp_status dp_plan_prepare_range(dp_plan* p, int64_t begin, int64_t end) {
     if (begin < 0 || end > p->P || begin > end)
         return fail(DP_ERR_RANGE, "range [%lld, %lld) not inside [0, %lld)", static_cast<long long>(begin),
                     static_cast<long long>(end), static_cast<long long>(p->P));
-    const DeviceTable* t = nullptr;
-    return range_table(p, begin, end, &t);
+    return ensure_full(p);  // a range needs no table of its own
 }
 
 // The state block and the statistics scratch, all or nothing: on a failure
@@ -672,15 +656,7 @@ static dp_status alloc_device_state(dp_plan* p) {
 
 dp_status dp_plan_drop_ranges(dp_plan* p) {
     if (!p) return fail(DP_ERR_INVALID_ARG, "dp_plan_drop_ranges: null plan");
-    if (p->ranges.empty()) return DP_OK;
-    dp_status s = ensure_device(p);
-    if (s != DP_OK) return s;
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize before freeing range tables");
-    for (const DeviceTable& t : p->ranges)
-        if (t.dev) (void)hipFree(t.dev);
-    p->ranges.clear();
-    return DP_OK;
+    return DP_OK;  // ranges hold no state of their own
 }
 
 dp_status dp_state_init(dp_plan* p, const dp_state_cfg* cfg, hipStream_t stream) {
@@ -1056,19 +1032,35 @@ dp_status dp_adam_step(dp_plan* p, const dp_adam_hparams* hp, int64_t begin, int
     if (s == DP_OK) s = need(&p->roles[DP_ROLE_PARAM][0], "PARAM");
     if (s != DP_OK) return s;
     if (begin == end) return DP_OK;
-    const DeviceTable* t = nullptr;
-    s = range_table(p, begin, end, &t);
+    s = ensure_full(p);
     if (s != DP_OK) return s;
     dpk::AdamArgs a{hp->lr, hp->eps, hp->weight_decay, p->cfg.beta1, p->cfg.beta2};
     const dpk::StateRefs sr = state_refs(p);
     const dpk::RoleRef pr = p->roles[DP_ROLE_PARAM][0].ref();
     const bool flat = all_flat(sr) && all_flat({gb->ref(), pr});
+    // No table of the range's own: flat pieces of [begin, end), or the pieces
+    // of the [0, P) table that overlap it, each clipped to it in the kernel
+    dpk::Table t;
+    dpk::PieceSpan sp;
+    if (flat) {
+        DeviceTable r;
+        r.begin = begin;
+        r.end = end;
+        r.log2s = p->full.log2s;
+        t = r.table(true);
+        sp = dpk::PieceSpan{0, t.npieces};
+    } else {
+        t = p->full.table(false);
+        t.begin = begin;
+        t.end = end;
+        sp = dpk::PieceSpan{piece_holding(p, begin), piece_holding(p, end - 1) + 1};
+    }
     Reads rd;
     rd.add(gbar_binding(p));
     rd.state(p);
     rd.add(&p->roles[DP_ROLE_PARAM][0]);
     return with_tables(p, rd, stream, "adamw launch", [&] {
-        return dpk::launch_adamw(p->pdt, t->table(flat), gb->ref(), sr, pr, p->state, a, stream);
+        return dpk::launch_adamw(p->pdt, t, sp, gb->ref(), sr, pr, p->state, a, stream);
     });
 }
 

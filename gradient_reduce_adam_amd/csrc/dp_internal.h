@@ -111,7 +111,10 @@ hipError_t launch_reduce(ReduceMode mode, dp_dtype gdt, int n, const Table& t, P
 hipError_t launch_stats(const Table& t, RoleRef gbar, StatsBuf sb, hipStream_t stream);
 hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* st, const ScalerArgs& args,
                            hipStream_t stream);
-hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& s, RoleRef p,
+// The update over pieces [p0, p1): flat pieces of the call's range, or the
+// pieces of the [0, P) table that overlap the range [t.begin, t.end), each
+// clipped to it.
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, PieceSpan sp, RoleRef gbar, const StateRefs& s, RoleRef p,
                         const DevState* st, const AdamArgs& args, hipStream_t stream);
 // Single pass: the replica average of launch_reduce (same sources, order and
 // statistics) feeding the update of every element, from the current bank into

@@ -94,6 +94,18 @@ __device__ __forceinline__ Piece piece_of(const Table& t, int64_t p) {
     return q;
 }
 
+// Piece p of the [0, P) chunk table with its elements clipped to the call's
+// range [t.begin, t.end): an update over a shard runs on the pieces of the
+// whole table that overlap the shard, so a shard needs no table of its own.
+// Over [0, P) the clip changes nothing.
+__device__ __forceinline__ Piece piece_of_clipped(const Table& t, int64_t p) {
+    Piece q = piece_of<false>(t, p);
+    const int64_t lo = t.begin - q.flat, hi = t.end - q.flat;
+    if (lo > q.vlo) q.vlo = lo < kPiece ? static_cast<int>(lo) : kPiece;
+    if (hi < q.vhi) q.vhi = hi > 0 ? static_cast<int>(hi) : 0;
+    return q;
+}
+
 template <typename T>
 __device__ __forceinline__ T* elem_ptr(const RoleRef& r, const Piece& q) {
     if (r.tab) return static_cast<T*>(r.tab[q.tensor]) + q.offset;
@@ -589,7 +601,7 @@ __global__ void __launch_bounds__(kWave) k_adamw(Table t, int64_t base, RoleRef 
     if (st->found_inf) return;
     const AdamCoef k = adam_coef(st->gscale, st->beta1_pow, st->beta2_pow, args);
     const int bank = st->bank;
-    const Piece q = piece_of<kFlat>(t, base + blockIdx.x);
+    const Piece q = kFlat ? piece_of<true>(t, base + blockIdx.x) : piece_of_clipped(t, base + blockIdx.x);
     const float* __restrict__ gp = elem_ptr<const float>(gbar, q);
     const StatePtrs sp(sr, pr, bank, bank, q);
     const LaneSpan l = lane_span(q);
@@ -786,9 +798,9 @@ hipError_t accumulate_all_t(dp_dtype gdt, bool first, int n, const Table& t, Pie
 }
 
 template <bool kFlat>
-hipError_t adamw_t(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& sr, RoleRef p, const DevState* st,
-                   const AdamArgs& args, hipStream_t s) {
-    return for_pieces(t.npieces, 1, [&](int64_t b, dim3 grid) {
+hipError_t adamw_t(dp_dtype pdt, const Table& t, PieceSpan sp, RoleRef gbar, const StateRefs& sr, RoleRef p,
+                   const DevState* st, const AdamArgs& args, hipStream_t s) {
+    return for_span(sp.p0, sp.p1, 1, [&](int64_t b, dim3 grid) {
         if (pdt == DP_BF16)
             hipLaunchKernelGGL((k_adamw<kFlat, 2>), grid, dim3(kWave), 0, s, t, b, gbar, sr, p, st, args);
         else
@@ -871,9 +883,11 @@ hipError_t launch_finalize(StatsBuf sb, int64_t nparts, FoldBuf fold, DevState* 
     return hipGetLastError();
 }
 
-hipError_t launch_adamw(dp_dtype pdt, const Table& t, RoleRef gbar, const StateRefs& sr, RoleRef p,
+hipError_t launch_adamw(dp_dtype pdt, const Table& t, PieceSpan sp, RoleRef gbar, const StateRefs& sr, RoleRef p,
                         const DevState* st, const AdamArgs& args, hipStream_t s) {
-    return t.flat ? adamw_t<true>(pdt, t, gbar, sr, p, st, args, s) : adamw_t<false>(pdt, t, gbar, sr, p, st, args, s);
+    if (sp.p0 < 0 || sp.p1 > t.npieces || sp.p0 > sp.p1) return hipErrorInvalidValue;
+    return t.flat ? adamw_t<true>(pdt, t, sp, gbar, sr, p, st, args, s)
+                  : adamw_t<false>(pdt, t, sp, gbar, sr, p, st, args, s);
 }
 
 hipError_t launch_reduce_adamw(ReduceMode mode, dp_dtype gdt, dp_dtype pdt, int n, const Table& t, PieceSpan sp,

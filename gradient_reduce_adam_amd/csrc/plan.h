@@ -90,14 +90,13 @@ struct dp_plan {
     dpapi::Binding roles[dpapi::kNumRoles][DP_MAX_REPLICAS];
     dpapi::EventPool events;  // of the per-tensor pointer-table rings
 
-    // device resources (allocated by dp_state_init / prepare / bind_tensors)
+    // device resources (allocated by the first GPU call: dp_state_init, prepare_range or bind_tensors)
     int device = -1;
     dpk::DevState* state = nullptr;
     dpk::StatsBuf stats{nullptr, nullptr};
     dpk::FoldBuf fold{nullptr, nullptr};
     dpapi::DeviceTable full;
     std::vector<dp_chunk> full_host;  // host copy of the [0, P) chunk table
-    std::vector<dpapi::DeviceTable> ranges;
 
     // ordering state
     bool state_ready = false;

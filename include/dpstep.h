@@ -215,16 +215,16 @@ dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* 
  * for example gradients in per-tensor buffers that change every step. */
 dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
 
-/* Builds and uploads the chunk table of [begin, end) so later dp_adam_step
- * calls on that range do not allocate (allocates; synchronises).  A range's
- * table stays cached until dp_plan_drop_ranges or dp_plan_destroy. */
+/* Checks that [begin, end) lies in [0, P) (DP_ERR_RANGE) and sets up the
+ * plan's device chunk table of [0, P) if no GPU call has done so yet (the
+ * plan's one-time set-up: allocates and synchronises then).  A shard range
+ * needs no table of its own: dp_adam_step runs on the pieces of the [0, P)
+ * table that overlap its range, clipped to it. */
 dp_status dp_plan_prepare_range(dp_plan* plan, int64_t begin, int64_t end);
 
-/* Frees the cached chunk tables of every range other than [0, P) (those of
- * dp_plan_prepare_range and of dp_adam_step calls), for callers whose shard
- * ranges change over a run.  Synchronises the device first, since launched
- * kernels may still read them; a later call on such a range builds its table
- * again.  Nothing else of the plan changes. */
+/* Does nothing and returns DP_OK: shard ranges hold no tables or other state
+ * of their own, so a caller whose shard ranges change over a run has nothing
+ * to release.  Kept so that such callers need no change. */
 dp_status dp_plan_drop_ranges(dp_plan* plan);
 
 /* The per-run scalar state of the step: the applied-step count t and the
@@ -360,8 +360,10 @@ dp_status dp_grad_stats(dp_plan* plan, int32_t scan, double max_norm, hipStream_
  * computed in binary64 and stored in binary32.  Nothing is written when the
  * finalised step was skipped.  Any partition of [0, P) into ranges gives the
  * same result as one call on [0, P).  DP_ERR_STATE if dp_grad_stats has not
- * run since the last accumulation or reduction.  The first call on a range
- * that dp_plan_prepare_range did not prepare allocates its table. */
+ * run since the last accumulation or reduction.  No range needs a table of
+ * its own, so no range allocates: with every role bound flat the launch
+ * covers the range's own pieces, otherwise the pieces of the [0, P) chunk
+ * table that overlap it, each clipped to the range. */
 dp_status dp_adam_step(dp_plan* plan, const dp_adam_hparams* hp, int64_t shard_begin, int64_t shard_end,
                        hipStream_t stream);
 

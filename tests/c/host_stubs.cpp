@@ -21,8 +21,8 @@ hipError_t launch_stats(const Table&, RoleRef, StatsBuf, hipStream_t) { return h
 hipError_t launch_finalize(StatsBuf, int64_t, FoldBuf, DevState*, const ScalerArgs&, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_adamw(dp_dtype, const Table&, RoleRef, const StateRefs&, RoleRef, const DevState*, const AdamArgs&,
-                        hipStream_t) {
+hipError_t launch_adamw(dp_dtype, const Table&, PieceSpan, RoleRef, const StateRefs&, RoleRef, const DevState*,
+                        const AdamArgs&, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_reduce_adamw(ReduceMode, dp_dtype, dp_dtype, int, const Table&, PieceSpan, const Srcs&,

@@ -337,6 +337,62 @@ def test_sharded_update_equals_unsharded_bitwise():
         assert np.array_equal(got_sh[k], got_full[k]), k
 
 
+def _bind_per_tensor(run, w):
+    """Binds every role of the run's plan through per-tensor pointer tables
+    into the same memory it holds, so the calls run on table pieces."""
+    d = run.d
+    off = [int(x) for x in w.offsets[:-1]]
+
+    def per(t):
+        return [t.data_ptr() + o * t.element_size() for o in off]
+
+    for b, (w_, m_, v_) in enumerate(d.banks):
+        for role, t in (("master", w_), ("exp_avg", m_), ("exp_avg_sq", v_)):
+            d.plan.bind_tensors(role, per(t), b)
+    d.plan.bind_tensors("param", per(d.param))
+    for r, t in enumerate(d.acc):
+        d.plan.bind_tensors("acc", per(t), r)
+    if d.gbar is not None and not (w.n == 1 and not w.partials):
+        d.plan.bind_tensors("gbar", per(d.gbar))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sharded_update_on_per_tensor_bindings(seed):
+    """With per-tensor bindings a shard's update runs on the pieces of the
+    whole chunk table that overlap it, clipped to the shard.  Seeded cuts
+    inside pieces, on tensor starts and one element past them, plus an empty
+    shard, give the bits of one unsharded call on flat bindings, and the
+    oracle's result."""
+    w = workloads.gpt2_small().with_(numel=RAGGED, n=2, a=2, max_norm=0.05, scaled_tensors=(1,), steps=3)
+    P = w.P
+    rng = np.random.default_rng(seed)
+    cuts = sorted({0, P, int(w.offsets[3]), int(w.offsets[5]) + 1, int(w.offsets[7]) - 3} |
+                  {int(x) for x in rng.integers(1, P, 9)})
+    shards = list(zip(cuts[:-1], cuts[1:])) + [(cuts[2], cuts[2])]
+    rng.shuffle(shards)
+    log(f"per-tensor shards, seed {seed}: {sorted(shards)}")
+    run = DeviceRun(w, shards=shards)
+    try:
+        _bind_per_tensor(run, w)
+        states = run.run(3)
+        got = run.window(0, P)
+    finally:
+        run.close()
+    run = DeviceRun(w)
+    try:
+        whole = run.run(3)
+        got_full = run.window(0, P)
+    finally:
+        run.close()
+    for k in ("w", "m", "v", "p"):
+        assert np.array_equal(got[k].view(np.uint8), got_full[k].view(np.uint8)), k
+    assert [x["t"] for x in states] == [x["t"] for x in whole]
+    ref = oracle_run(w, 3)
+    for s_, (g, r) in enumerate(zip(states, ref.scalars), start=1):
+        assert_scalars_match(g, r, where=f"step {s_}")
+    assert_state_close(got, ref.state[(0, P)], ulp_bound(w), where="per-tensor shards")
+
+
 def test_bitwise_reproducible():
     w = workloads.gpt2_small().with_(numel=RAGGED, n=8, a=2, max_norm=0.05, scaled_tensors=(3,), steps=2)
     outs = []
