@@ -387,14 +387,37 @@ Reads reduction_reads(dp_plan* p, dpk::ReduceMode mode) {
     return rd;
 }
 
+// Under HIP graph capture the per-tensor tables a launch reads must already
+// have been uploaded by an uncaptured call: a captured upload would copy the
+// staging slot at every replay, after later rebindings rewrote it, and an
+// event recorded during a capture marks nothing on the stream itself.  So a
+// captured call whose tables are pending fails, and its reads are not
+// tracked (a plan whose calls were captured must not rebind those roles
+// while the graph may replay).  The upload is prior work like any other the
+// graph reads: the caller orders the replays after it.
+dp_status tables_ready_for_capture(const Reads& rd) {
+    for (int i = 0; i < rd.n; ++i) {
+        const Binding& b = *rd.b[i];
+        if (b.bound && b.dev_table && b.pending)
+            return fail(DP_ERR_STATE,
+                        "a per-tensor pointer table rebound since the last uncaptured call would be uploaded inside a "
+                        "graph capture; make one uncaptured call that reads it first");
+    }
+    return DP_OK;
+}
+
 // A launch that reads per-tensor tables: stage them, launch, note the reads.
 template <typename F>
 dp_status with_tables(dp_plan* p, const Reads& rd, hipStream_t stream, const char* what, F&& launch) {
-    dp_status s = stage_tables(p, rd, stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    const bool capturing = cs != hipStreamCaptureStatusNone;
+    dp_status s = capturing ? tables_ready_for_capture(rd) : stage_tables(p, rd, stream);
     if (s != DP_OK) return s;
     s = check_launch(launch(), what);
     if (s != DP_OK) return s;
-    return note_reads(p, rd, stream);
+    return capturing ? DP_OK : note_reads(p, rd, stream);
 }
 
 // Slot k may be written again once its upload and every launch that read it

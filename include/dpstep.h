@@ -212,7 +212,12 @@ dp_status dp_plan_bind_flat(dp_plan* plan, dp_role role, int32_t replica, void* 
  * only four rebindings later, after the launches that read it have finished
  * (the rebinding waits for them then, if they have not).  Rebinding the
  * pointers already bound does nothing.  Suited to rebinding per micro-step,
- * for example gradients in per-tensor buffers that change every step. */
+ * for example gradients in per-tensor buffers that change every step.
+ * Under HIP graph capture a call must find its tables uploaded by an earlier
+ * uncaptured call (DP_ERR_STATE otherwise: make one uncaptured call after
+ * rebinding; replays are then ordered after it like after any prior work),
+ * and roles whose calls were captured must not be rebound while the graph
+ * may replay, since the graph reads the tables current at capture. */
 dp_status dp_plan_bind_tensors(dp_plan* plan, dp_role role, int32_t replica, void* const* ptrs);
 
 /* Checks that [begin, end) lies in [0, P) (DP_ERR_RANGE) and sets up the
