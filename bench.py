@@ -31,6 +31,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 RESIDENT_GRAD_BUDGET = 80e9  # bytes of pre-generated gradients kept in HBM
 CPU_BASELINE_SECONDS = 10.0  # oracle work timed for each leg of the CPU baseline
+EVENT_RECORD_US = 4.0  # host time of one timing-event record on the step's stream (ROCm 7, MI355X host)
+EVENT_BUDGET = 0.02  # the share of the timed region the timing events may cost
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = (os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "kernels.hip"),
               os.path.join(ROOT, "gradient_reduce_adam_amd", "csrc", "dp_internal.h"))
@@ -94,7 +96,10 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/traffic.json, then exit")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("need --steps >= 1 and --warmup >= 0")
+    return args
 
 
 # rocprofv3 kernel names of each call kind (regular expressions on the
@@ -216,6 +221,17 @@ def kernel_source_hash() -> str:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def event_stride(step_s: Optional[float], records: int) -> int:
+    """Every stride-th timed step carries `records` timing events (one at its
+    start and one after each call), so that the events cost at most
+    EVENT_BUDGET of the timed region: a launch-bound step of tens of
+    microseconds would otherwise be slowed by its own events, while a step of
+    a few milliseconds or more carries them on every step."""
+    if not step_s or step_s <= 0:
+        return 1
+    return max(1, math.ceil(records * EVENT_RECORD_US * 1e-6 / (EVENT_BUDGET * step_s)))
 
 
 def single_pass_for(w, update: str) -> bool:
@@ -505,59 +521,73 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         else:
             dp_plan_bind_flat(plan.handle, DP_ROLE_GRAD, r, a)
 
-    events = {}
-    sink = [events]  # where timed() records: the timed run's events, or one logged step's
+    last = 1 if w.partials else w.a
+    ncalls = (last - 1) + (1 if single else 3)
 
-    def timed(kind, fn, rec):
-        if rec:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(st_obj)
-            fn()
-            e1.record(st_obj)
-            sink[0].setdefault(kind, []).append((e0, e1))
-        else:
-            fn()
+    def one_step(marks=None):
+        """Issues one step.  With `marks` (ncalls + 1 events) it records
+        marks[0] at the start and marks[i + 1] after call i, so call i is timed
+        from marks[i] to marks[i + 1] and the step from the first to the last.
+        Returns the kinds of the calls in order."""
+        kinds = []
 
-    def one_step(rec: bool):
-        last = 1 if w.partials else w.a
+        def call(kind, fn):
+            fn()
+            kinds.append(kind)
+            if marks is not None:
+                marks[len(kinds)].record(st_obj)
+
+        if marks is not None:
+            marks[0].record(st_obj)
         for k in range(1, last):
             for r in range(w.n):
                 bind_grad(r, addr[(r, k)])
-            timed("accumulate_first" if k == 1 else "accumulate",
-                  lambda k=k: plan.accumulate_all(first=(k == 1), stream=stream), rec)
+            call("accumulate_first" if k == 1 else "accumulate",
+                 lambda k=k: plan.accumulate_all(first=(k == 1), stream=stream))
         for r in range(w.n):
             bind_grad(r, addr[(r, last)])
         if single:  # one call: the single-pass kernel, the statistics fold and the (idle) parameter restore
-            timed("reduce_adamw", lambda: plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
-            return
-        timed("accumulate_reduce", lambda: plan.accumulate_reduce(stream=stream), rec)
-        timed("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream), rec)
+            call("reduce_adamw", lambda: plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=stream))
+            return kinds
+        call("accumulate_reduce", lambda: plan.accumulate_reduce(stream=stream))
+        call("finalize", lambda: plan.grad_stats(scan=False, max_norm=w.max_norm, stream=stream))
         if d.offload == "staged":
-            timed("adamw", d.staged_update, rec)
+            call("adamw", d.staged_update)
         else:
-            timed("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream), rec)
+            call("adamw", lambda: plan.adam_step(w.lr, w.eps, w.weight_decay, stream=stream))
+        return kinds
 
+    def new_marks():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
+
+    # warm-up, each step timed on the host: the shortest sets the event stride
+    warm_s = []
     for _ in range(warmup):
-        one_step(False)
+        t0 = time.perf_counter()
+        one_step()
+        torch.cuda.synchronize()
+        warm_s.append(time.perf_counter() - t0)
+    stride = event_stride(min(warm_s) if warm_s else None, ncalls + 1)
+    marks = {i: new_marks() for i in range(0, steps, stride)}
+    for m in marks.values():  # each event created and recorded once before the timed region
+        for e in m:
+            e.record(st_obj)
     torch.cuda.synchronize()
-    step_marks = []  # each timed step between two events on the library's stream
     t0 = time.perf_counter()
-    for _ in range(steps):
-        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        m0.record(st_obj)
-        one_step(True)
-        m1.record(st_obj)
-        step_marks.append((m0, m1))
+    for i in range(steps):
+        kinds = one_step(marks.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_ms = sorted(a.elapsed_time(b) for a, b in step_marks)
+    step_ms = sorted(m[0].elapsed_time(m[-1]) for m in marks.values())
+    events = {}
+    for m in marks.values():
+        for j, kind in enumerate(kinds):
+            events.setdefault(kind, []).append((m[j], m[j + 1]))
     skipped_ms = None
     if w.injections and not graph:
         # one step whose g_bar holds an inf, as the workload injects one: the
         # step is skipped (single pass: computed, then discarded and the
         # parameters emitted again); the buffer is restored afterwards
-        last = 1 if w.partials else w.a
         _, r0, _, idx, val = w.injections[0]
         ptr = addr[(r0 % w.n, last)] + 2 * idx
         flat = ring.view(-1)
@@ -565,19 +595,17 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         saved = flat[pos].clone()
         torch.cuda.synchronize()
         synth._poke_u16(ptr, synth._lp_bits(val, w.grad_dtype), stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st_obj)
-        one_step(False)
-        e1.record(st_obj)
+        m = new_marks()
+        one_step(m)
         torch.cuda.synchronize()
-        skipped_ms = e0.elapsed_time(e1)
+        skipped_ms = m[0].elapsed_time(m[-1])
         assert d.read_state()["found_inf"] == 1
         flat[pos] = saved
         torch.cuda.synchronize()
     if graph:  # the same step as one HIP graph: capture, warm up, time the replays
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st_obj):
-            one_step(False)
+            one_step()
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -590,15 +618,16 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     if log_path:  # per-step records, outside everything timed above
         with open(log_path, "w") as f:
             for _ in range(steps):
-                sink[0] = {}
-                one_step(True)
+                m = new_marks()
+                kinds = one_step(m)
                 s_ = d.read_state()  # synchronises the stream
-                ms = {k: sum(a.elapsed_time(b) for a, b in v) for k, v in sink[0].items()}
+                ms = {}
+                for j, kind in enumerate(kinds):
+                    ms[kind] = ms.get(kind, 0.0) + m[j].elapsed_time(m[j + 1])
                 f.write(json.dumps({"workload": w.name, "t": s_["t"], "iter": s_["iter"], "found_inf": s_["found_inf"],
                                     "scale": s_["scale"], "norm": s_["norm"], "clip": s_["clip"], "call_ms": ms,
                                     "step_ms": sum(ms.values()),
                                     "params_per_s": w.P / (sum(ms.values()) * 1e-3)}) + "\n")
-        sink[0] = events
     ckpt = measure_checkpoint(d, ckpt_dir) if ckpt_dir else None
     per_kind = {}
     for kind, pairs in events.items():
@@ -609,7 +638,9 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     del bufs, ring, spacer_buf
     torch.cuda.empty_cache()
     per_kind["skipped_step_ms"] = skipped_ms
-    per_kind["step_ms"] = None if graph else step_ms  # the eager steps; a graph replays them as one
+    per_kind["step_ms"] = None if graph else step_ms  # the instrumented eager steps; a graph replays them as one
+    per_kind["event_stride"] = stride
+    per_kind["instrumented_steps"] = len(marks)
     return elapsed, per_kind, state, ckpt, used_layout
 
 
@@ -893,6 +924,8 @@ def main():
 
     skipped_ms = per_kind.pop("skipped_step_ms", None)
     step_ms = per_kind.pop("step_ms", None)
+    stride = per_kind.pop("event_stride", None)
+    instrumented = per_kind.pop("instrumented_steps", None)
     # dominant kernel: the call kind that moves the most algorithmic bytes per step
     dom = max(per_param, key=lambda k: per_param[k])
     dom_bytes = launch_bytes(w, dom, single)
@@ -948,7 +981,10 @@ def main():
                                         "this workload (profiles/traffic.json), scaled by the same counters on a "
                                         "plain copy; valid for the kernel source it was taken on (hash checked)"
                                         if traffic is not None else None)},
-        "breakdown_ms_per_step": {k: v["total_ms"] / args.steps for k, v in per_kind.items()},
+        # per-call times of the eager timed steps that carried events
+        "breakdown_ms_per_step": {k: v["total_ms"] / instrumented for k, v in per_kind.items()},
+        "event_stride": stride,
+        "instrumented_steps": instrumented,
         "final_state": {"t": state["t"], "norm": state["norm"], "found_inf": state["found_inf"]},
         "skipped_step_ms": skipped_ms,
         # per-step event times of the timed steps: the median and the fastest

@@ -343,12 +343,9 @@ dp_status stage_tables(dp_plan* p, const Reads& rd, hipStream_t stream) {
     return DP_OK;
 }
 
-// After a launch on `stream`: one event behind it, held by every per-tensor
-// table slot the launch read.
+// After a launch on `stream` that read at least one per-tensor table: one event
+// behind it, held by every per-tensor table slot the launch read.
 dp_status note_reads(dp_plan* p, const Reads& rd, hipStream_t stream) {
-    bool any = false;
-    for (int i = 0; i < rd.n && !any; ++i) any = rd.b[i]->bound && rd.b[i]->dev_table;
-    if (!any) return DP_OK;
     int ev = -1;
     hipError_t e = ev_take(p, &ev);
     if (e == hipSuccess) e = hipEventRecord(p->events.ev[ev], stream);
@@ -407,8 +404,12 @@ dp_status tables_ready_for_capture(const Reads& rd) {
 }
 
 // A launch that reads per-tensor tables: stage them, launch, note the reads.
+// A launch that reads no per-tensor table (flat bindings) skips all of it.
 template <typename F>
 dp_status with_tables(dp_plan* p, const Reads& rd, hipStream_t stream, const char* what, F&& launch) {
+    bool tables = false;
+    for (int i = 0; i < rd.n && !tables; ++i) tables = rd.b[i]->bound && rd.b[i]->dev_table;
+    if (!tables) return check_launch(launch(), what);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(stream, &cs);
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");

@@ -74,3 +74,14 @@ def test_cpu_share(tmp_path, monkeypatch):
     assert bench.cpu_share(str(cpu_max))["threads"] == 64
     monkeypatch.setenv("OMP_NUM_THREADS", "8")
     assert bench.cpu_share(str(cpu_max))["threads"] == 8
+
+
+def test_event_stride():
+    # timing events cost at most about 2% of the timed region: a step of a
+    # few milliseconds carries them on every step, a 40 us step on few
+    assert bench.event_stride(None, 3) == 1
+    assert bench.event_stride(0.1, 9) == 1
+    assert bench.event_stride(1e-3, 11) == 3
+    assert bench.event_stride(2.5e-3, 11) == 1
+    s = bench.event_stride(40e-6, 3)
+    assert s == 15 and 3 * bench.EVENT_RECORD_US * 1e-6 / (s * 40e-6) <= bench.EVENT_BUDGET

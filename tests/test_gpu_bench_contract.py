@@ -37,8 +37,9 @@ def test_bench_prints_the_contract_line(tmp_path):
     assert rf["traffic"] is None or rf["traffic"] > 0
     mc = d["measured_ceilings"]
     assert mc["copy_gbps"] > 0 and mc["read_gbps"] > 0 and mc["runtime_copy_gbps"] > 0
-    # per-step event times beside the wall-clock mean
+    # per-step event times beside the wall-clock mean, on every stride-th step
     assert 0 < d["step_ms_min"] <= d["step_ms_median"]
+    assert d["event_stride"] >= 1 and d["instrumented_steps"] == len(range(0, 3, d["event_stride"]))
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["unit"] == d["unit"]
     assert isinstance(cb["sample"], str) and cb["sample"]
