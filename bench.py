@@ -679,20 +679,22 @@ def run_overlap(w, steps: int, warmup: int, bucket_mbs, tokens: int, single: boo
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    # the two parts alone: one micro-step's backward, and the last micro-step's reduction
+    # the two parts alone, each after one untimed call: one micro-step's
+    # backward, and the last micro-step's reduction
     last = 1 if w.partials else w.a
+    produce(1, last, 0, w.P, st)
     t_bwd = timed(lambda: produce(1, last, 0, w.P, st), 3)
     for r, a_ in enumerate(addrs):
         driver.dp_plan_bind_flat(d.plan.handle, driver.DP_ROLE_GRAD, r, a_)
     reds = []
-    for _ in range(3):  # the last micro-step's reduction as the step issues it (after earlier micro-steps)
+    for _ in range(4):  # the last micro-step's reduction as the step issues it (after earlier micro-steps)
         if last > 1:
             d.plan.accumulate_all(first=True, stream=st)
         if single:  # the reduction, the statistics and the update in one pass
             reds.append(timed(lambda: d.plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=st), 1))
         else:
             reds.append(timed(lambda: d.plan.accumulate_reduce(stream=st), 1))
-    t_red = sum(reds) / len(reds)
+    t_red = statistics.median(reds[1:])
     d.close()
     del d
     torch.cuda.empty_cache()
