@@ -103,14 +103,53 @@ class DeviceRun:
 # oracle side
 # ----------------------------------------------------------------------------
 def oracle_run(w, steps: int, windows=None, keep_gbar=(), chunk: int = 1 << 20, progress=None):
+    """The oracle's run of workload w; with clipping, each window's state also
+    carries ``m_slack`` (see ``m_slack``)."""
     def grad_fn(step, r, k, lo, hi, scale):
         return synth.grad_host(w, step, r, k, lo, hi, scale)
 
     def master_fn(lo, hi):
         return synth.master_host(w, lo, hi)
 
-    return oracle.run(w, steps, grad_fn, master_fn, windows=windows, threads=THREADS, chunk=chunk,
-                      keep_gbar=keep_gbar, progress=progress)
+    extra = set(range(1, steps + 1)) - set(keep_gbar) if w.max_norm > 0 else set()
+    res = oracle.run(w, steps, grad_fn, master_fn, windows=windows, threads=THREADS, chunk=chunk,
+                     keep_gbar=tuple(sorted(set(keep_gbar) | extra)), progress=progress)
+    if w.max_norm > 0:
+        for win, st in res.state.items():
+            per_step = [(res.gbar[s][win], rec) for s, rec in enumerate(res.scalars, start=1)]
+            st["m_slack"] = m_slack(w.P, w.beta1, per_step)
+        for s in extra:
+            res.gbar.pop(s, None)
+    return res
+
+
+def m_slack(P: int, beta1: float, steps) -> np.ndarray:
+    """How far m may legitimately differ from the oracle's under clipping, per
+    element, from the oracle's own per-step g_bar and scalars.
+
+    The global norm is a binary64 sum of P non-negative squares whose order
+    "Distributed Training: Split along the Four Axes of Data, Tensor, Pipeline,
+    and State" leaves open (its reduction-order paragraph).  Two orders agree
+    to (P - 1) * 2^-53 relative (the recursive-summation bound), so the clip
+    factor and every g = g_bar * gscale may differ by delta = (P + 8) * 2^-53
+    relative (a few more roundings in the square root and the division).
+    Each step's m, stored in binary32, may then round to a neighbouring value:
+    one ulp, at most 2^-23 * max|g| since |m_s| <= max_{r<=s} |g_r|.  Both
+    carry over with weight beta1 per step, so
+        |dm_t| <= sum_s beta1^(t-s) * ((1 - beta1) * delta * |g_s| + ulp(m_s))
+               <= (delta + 2^-23 / (1 - beta1)) * max_s |g_s|.
+    Where m nearly cancels, this exceeds 64 binary32 ulp of m itself; w and v
+    have no such cancellation.  Skipped steps (found_inf) do not touch m."""
+    delta = (P + 8) * 2.0 ** -53
+    bound = (delta + 2.0 ** -23 / (1.0 - beta1)) * 1.01
+    gmax = None
+    for gbar, rec in steps:
+        if gmax is None:
+            gmax = np.zeros(gbar.size, np.float64)
+        if rec["found_inf"]:
+            continue
+        np.maximum(gmax, np.abs(gbar.astype(np.float64) * rec["gscale"]), out=gmax)
+    return bound * gmax if gmax is not None else np.zeros(0, np.float64)
 
 
 # ----------------------------------------------------------------------------
@@ -136,7 +175,9 @@ def assert_state_close(got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], m
                        where: str = "") -> dict:
     """master, m and v within the stated tolerance and within max_ulp binary32
     ulp of the oracle (finite pairs; a non-finite value must match its own
-    kind); the low-precision parameters within 1 ulp.  Returns the largest
+    kind); the low-precision parameters within 1 ulp.  Under clipping an
+    element of m beyond max_ulp passes if it lies within ``ref["m_slack"]``,
+    the difference the norm's summation order allows.  Returns the largest
     ulp distance of each."""
     report = {}
     for key in ("w", "m", "v"):
@@ -157,7 +198,12 @@ def assert_state_close(got: Dict[str, np.ndarray], ref: Dict[str, np.ndarray], m
                               f"gpu {g[bad[:5]]} oracle {r[bad[:5]]}"
         u = np.where(fin, ulps32(g, r), 0)
         report[key + "_max_ulp"] = int(u.max()) if g.size else 0
-        far = np.flatnonzero(u > max_ulp)
+        far_mask = u > max_ulp
+        if key == "m" and "m_slack" in ref:  # clipping: the norm's summation order (see m_slack)
+            within = far_mask & (err <= ref["m_slack"])
+            report["m_within_norm_order_slack"] = int(np.count_nonzero(within))
+            far_mask &= ~within
+        far = np.flatnonzero(far_mask)
         assert far.size == 0, f"{where} {key}: {far.size} elements more than {max_ulp} ulp from the oracle " \
                               f"(max {report[key + '_max_ulp']}), first at {far[:5]}: gpu {g[far[:5]]} " \
                               f"oracle {r[far[:5]]}"

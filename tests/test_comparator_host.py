@@ -1,11 +1,13 @@
 """The tolerance comparison the GPU parity tests use (gpu_common), on the
 CPU: values within the stated tolerance pass, values outside it fail, a
-non-finite value matches only a non-finite value of the same kind, and the
-binary32 ulp bound catches what the absolute floor lets through."""
+non-finite value matches only a non-finite value of the same kind, the
+binary32 ulp bound catches what the absolute floor lets through, and under
+clipping m may differ by what the norm's summation order allows, no more."""
 import numpy as np
 import pytest
 
-from gpu_common import MAX_ULP_CLIPPED, assert_state_close
+from gpu_common import MAX_ULP_CLIPPED, assert_state_close, oracle_run, ulps32
+from test_gpu_random_configs import _draw
 
 LOOSE = 1 << 30  # ulp bound that never binds: the stated tolerance alone
 
@@ -96,3 +98,39 @@ def test_nonfinite_pairs_are_not_ulp_counted():
     a = np.array([np.nan], np.float32)
     b = np.array([0x7FC00001], np.uint32).view(np.float32)
     assert_state_close(_state(a), _state(b), 0, where="nan payloads")
+
+
+def test_m_slack_exempts_only_m_and_only_within_it():
+    ref = _state([1e-13, 0.01, 0.02])
+    ref["m_slack"] = np.array([1e-18, 1e-18, 1e-18])
+    got = _state([1e-13, 0.01, 0.02])
+    got["m"][0] = _up(np.float32(1e-13), 200)  # 200 ulp, 1.3e-18 absolute: beyond the slack
+    with pytest.raises(AssertionError, match="ulp"):
+        assert_state_close(got, ref, MAX_ULP_CLIPPED, where="beyond slack")
+    got["m"][0] = _up(np.float32(1e-13), 100)  # 100 ulp, 6.3e-19 absolute: within it
+    rep = assert_state_close(got, ref, MAX_ULP_CLIPPED, where="within slack")
+    assert rep["m_max_ulp"] == 100 and rep["m_within_norm_order_slack"] == 1
+    got["w"][0] = got["m"][0]  # the same difference in w is not exempt
+    with pytest.raises(AssertionError, match="w: 1 elements more than"):
+        assert_state_close(got, ref, MAX_ULP_CLIPPED, where="w")
+
+
+def test_m_slack_covers_the_norms_summation_order():
+    """The oracle against itself with the norm's binary64 sum taken in
+    another order (chunks of 777 elements instead of 2^20), on a clipped
+    configuration of the random sweep (5 partials, clip 1.0, a NaN that skips
+    step 1) where m nearly cancels at one element: there m moves by more than
+    64 ulp, everywhere it stays within the slack, and w and v stay within the
+    ulp bound."""
+    w, *_ = _draw(1851)
+    a = oracle_run(w, w.steps)
+    b = oracle_run(w, w.steps, chunk=777)
+    A, B = a.state[(0, w.P)], b.state[(0, w.P)]
+    assert any(x["norm"] != y["norm"] for x, y in zip(a.scalars, b.scalars))  # the orders differ
+    u = ulps32(A["m"], B["m"])
+    assert u.max() > MAX_ULP_CLIPPED
+    d = np.abs(A["m"].astype(np.float64) - B["m"].astype(np.float64))
+    assert np.all(d <= A["m_slack"]) and np.all(d <= B["m_slack"])
+    for k in ("w", "v"):
+        assert ulps32(A[k], B[k]).max() <= MAX_ULP_CLIPPED, k
+    assert_state_close(B, A, MAX_ULP_CLIPPED, where="two norm orders")
