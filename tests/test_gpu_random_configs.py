@@ -52,7 +52,9 @@ def _draw(seed):
     return w, chunk, single, shards, location
 
 
-@pytest.mark.parametrize("seed", range(32))
+# 1851 and 3044: clipped draws where m nearly cancels at one or two
+# elements, beyond 64 ulp and within the norm-order slack (gpu_common.m_slack)
+@pytest.mark.parametrize("seed", list(range(32)) + [1851, 3044])
 def test_random_configuration_matches_oracle(seed):
     w, chunk, single, shards, location = _draw(seed)
     log(f"seed {seed}: P={w.P} T={w.T} n={w.n} a={w.a} {w.grad_dtype}/{w.param_dtype} clip={w.max_norm} "
