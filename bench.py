@@ -606,12 +606,16 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st_obj):
             one_step()
-        for _ in range(warmup):
-            g.replay()
+        # replayed on the step's stream, like the eager steps (torch replays
+        # on the current stream)
+        with torch.cuda.stream(st_obj):
+            for _ in range(warmup):
+                g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
+        with torch.cuda.stream(st_obj):
+            for _ in range(steps):
+                g.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     state = d.read_state()

@@ -87,6 +87,22 @@ def even_shards(P: int, shards: int) -> List[Tuple[int, int]]:
     return [(cuts[i], cuts[i + 1]) for i in range(shards)]
 
 
+class StepGraph:
+    """A step captured into a HIP graph.  ``replay`` launches it on the step's
+    own stream, so a replay is ordered after the work issued there before it
+    (new gradients written on that stream) and before the work issued after
+    it (``read_state``, the next gradients).  torch's own ``replay`` launches
+    on the current stream, which is not ordered with the step's stream."""
+
+    def __init__(self, graph: "torch.cuda.CUDAGraph", stream: "torch.cuda.Stream"):
+        self.graph = graph
+        self.stream = stream
+
+    def replay(self) -> None:
+        with torch.cuda.stream(self.stream):
+            self.graph.replay()
+
+
 class DPStep:
     def __init__(self, numel: Sequence[int], n: int, a: int, grad_dtype: str, param_dtype: str, *,
                  lr: float = 1e-3, eps: float = 1e-8, weight_decay: float = 0.01, beta1: float = 0.9,
@@ -424,7 +440,7 @@ class DPStep:
             pl.accumulate_reduce(stream=st)
         self.finish()
 
-    def capture_step(self, grad_slots: Sequence[Sequence[int]]) -> "torch.cuda.CUDAGraph":
+    def capture_step(self, grad_slots: Sequence[Sequence[int]]) -> "StepGraph":
         """Captures ``issue_fixed`` into a HIP graph on this step's stream
         (which must not be the null stream).  Each replay runs one more step on
         whatever the gradient buffers then hold; the plan's host-side call
@@ -435,7 +451,7 @@ class DPStep:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=self.stream):
             self.issue_fixed(grad_slots)
-        return g
+        return StepGraph(g, self.stream)
 
     def read_state(self) -> dict:
         return self.plan.read_state(stream=self.stream.cuda_stream)

@@ -1,6 +1,7 @@
 """One whole step captured into a HIP graph and replayed: every replay,
 with the program's own eager work (new gradients, a state read-back) in
-between, gives the same bits as the eager step sequence."""
+between, gives the same bits as the eager step sequence.  Replays launch on
+the step's stream, so that work is ordered around them."""
 import numpy as np
 import pytest
 import torch
@@ -20,24 +21,31 @@ CASES = {
     "clip_dynamic_skip": (dict(base="gpt2_small", numel=(3000, 17, 70001, 4096), n=3, a=2, max_norm=0.05,
                                scaled_tensors=(2,), scaler="dynamic", init_scale=1024.0, growth_interval=2,
                                injections=((3, 1, 2, 3100, float("inf")),)), False),
+    # the state in pinned host memory: a replay that reads it across PCIe
+    # takes long enough that a read of the state not ordered after it sees
+    # the previous step
+    "host_state_single_pass": (dict(base="tiny", numel=(65536 * 3 + 7, 4099), n=16, a=3, scaler="dynamic",
+                                    init_scale=1024.0, growth_interval=2,
+                                    injections=((1, 8, 1, 67706, float("inf")),)), True, "host"),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_graph_replays_equal_eager_steps(name):
-    spec, single = CASES[name]
+    spec, single, *where = CASES[name]
+    location = where[0] if where else "hbm"
     spec = dict(spec)
     w = workloads.by_name(spec.pop("base")).with_(**spec)
     steps = 5
-    log(f"graph {name}: P={w.P} n={w.n} a={w.a} single_pass={single}")
-    eager = DeviceRun(w, single_pass=single)
+    log(f"graph {name}: P={w.P} n={w.n} a={w.a} single_pass={single} state={location}")
+    eager = DeviceRun(w, single_pass=single, state_location=location)
     try:
         ref_states = eager.run(steps)
         ref = eager.window(0, w.P)
     finally:
         eager.close()
     last = 1 if w.partials else w.a
-    run = DeviceRun(w, single_pass=single, stream=torch.cuda.Stream())
+    run = DeviceRun(w, single_pass=single, stream=torch.cuda.Stream(), state_location=location)
     d, st = run.d, run.d.stream.cuda_stream
     bufs = [[torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)] for _ in range(last)]
     slots = [[b.data_ptr() for b in row] for row in bufs]
