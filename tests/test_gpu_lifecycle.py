@@ -222,3 +222,125 @@ def test_rebound_tables_read_from_two_streams():
         want = want + g[k].float()
     log(f"{len(buckets)} buckets on two streams, {micro} rebound micro-steps")
     assert torch.equal(acc.view(torch.int32), want.view(torch.int32))
+
+
+def _bind_every_role_per_tensor(d, w):
+    off = [int(x) for x in w.offsets[:-1]]
+
+    def per(t):
+        return [t.data_ptr() + o * t.element_size() for o in off]
+
+    for b, (w_, m_, v_) in enumerate(d.banks):
+        for role, t in (("master", w_), ("exp_avg", m_), ("exp_avg_sq", v_)):
+            d.plan.bind_tensors(role, per(t), b)
+    d.plan.bind_tensors("param", per(d.param))
+    for r, t in enumerate(d.acc):
+        d.plan.bind_tensors("acc", per(t), r)
+    if d.gbar is not None and not (w.n == 1 and not w.partials):
+        d.plan.bind_tensors("gbar", per(d.gbar))
+
+
+CALLS_ON_STREAMS = {
+    0: dict(numel=(3000, 0, 17, 70001, 4096, 257), n=3, a=3, max_norm=0.05, scaled_tensors=(3,), single=False,
+            shards=[(0, 40000), (40000, 77371)]),
+    1: dict(numel=(65536, 5, 12289), n=4, a=4, max_norm=0.0, scaled_tensors=(), single=True, shards=None),
+    2: dict(numel=(100, 30000, 1, 30000), n=16, a=2, max_norm=1.0, scaled_tensors=(1,), single=False, shards=None,
+            scaler="dynamic", init_scale=1024.0, growth_interval=2, injections=((2, 5, 2, 30050, float("inf")),)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CALLS_ON_STREAMS))
+def test_calls_on_random_streams_with_per_tensor_tables(case):
+    """Every call of a step on a seeded random one of three streams, the data
+    dependencies between calls ordered by the caller's events, every role
+    bound per tensor and the gradients rebound per tensor before every
+    micro-step across two buffers per replica (so table uploads happen on one
+    stream and are read on others, and ring slots are reused while other
+    streams hold them): the same bits as the flat run on one stream."""
+    spec = dict(CALLS_ON_STREAMS[case])
+    single, shards = spec.pop("single"), spec.pop("shards")
+    w = workloads.gpt2_small().with_(steps=3, **spec)
+    rng = np.random.default_rng(900 + case)
+    log(f"calls on streams {case}: P={w.P} T={w.T} n={w.n} a={w.a} single={single} shards={shards}")
+
+    def make():
+        return driver.DPStep(w.numel, w.n, w.a, w.grad_dtype, w.param_dtype, lr=w.lr, eps=w.eps,
+                             weight_decay=w.weight_decay, beta1=w.beta1, beta2=w.beta2, max_norm=w.max_norm,
+                             scaler=w.scaler, init_scale=w.init_scale, backoff=w.backoff, growth=w.growth,
+                             growth_interval=w.growth_interval, shards=shards, single_pass=single)
+
+    def window(d):
+        torch.cuda.synchronize()
+        w_, m_, v_ = d.state_tensors()
+        return [x.view(torch.uint8).cpu().numpy() for x in (w_, m_, v_, d.param)]
+
+    slots = [torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(w.n)]
+    d = make()
+    d.set_master(lambda ptr: synth.master_device(w, ptr, d.stream.cuda_stream))
+
+    def produce(step, r, k, scale):
+        synth.grad_device(w, step, r, k, slots[r].data_ptr(), scale, d.stream.cuda_stream)
+        return slots[r].data_ptr()
+
+    try:
+        ref_states = [d.step(produce) for _ in range(w.steps)]
+        ref = window(d)
+    finally:
+        d.close()
+
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    off = [int(x) for x in w.offsets[:-1]]
+    bufs = [[torch.empty(w.P, dtype=torch.int16, device="cuda") for _ in range(2)] for _ in range(w.n)]
+    d = make()
+    d.set_master(lambda ptr: synth.master_device(w, ptr, d.stream.cuda_stream))
+    _bind_every_role_per_tensor(d, w)
+    prev = torch.cuda.Event()
+    prev.record(d.stream)
+
+    def on_random_stream():
+        s = streams[int(rng.integers(0, 3))]
+        s.wait_event(prev)
+        return s
+
+    def done(s):
+        ev = torch.cuda.Event()
+        ev.record(s)
+        return ev
+
+    states = []
+    try:
+        for step in range(1, w.steps + 1):
+            for k in range(1, w.a + 1):
+                s = on_random_stream()
+                for r in range(w.n):
+                    b = bufs[r][k & 1]
+                    synth.grad_device(w, step, r, k, b.data_ptr(), d.scale, s.cuda_stream)
+                    d.plan.bind_tensors("grad", [b.data_ptr() + 2 * o for o in off], r)
+                if k < w.a:
+                    d.plan.accumulate_all(first=(k == 1), stream=s.cuda_stream)
+                elif single:
+                    d.plan.reduce_adam_step(w.lr, w.eps, w.weight_decay, stream=s.cuda_stream)
+                else:
+                    d.plan.accumulate_reduce(stream=s.cuda_stream)
+                prev = done(s)
+            if not single:
+                s = on_random_stream()
+                d.plan.grad_stats(scan=False, max_norm=w.max_norm, stream=s.cuda_stream)
+                prev = done(s)
+                for b_, e_ in (shards or [(0, w.P)]):
+                    s = on_random_stream()
+                    d.plan.adam_step(w.lr, w.eps, w.weight_decay, b_, e_, stream=s.cuda_stream)
+                    prev = done(s)
+            d.stream.wait_event(prev)
+            st = d.read_state()
+            d.scale = st["scale"]
+            states.append(st)
+            prev = done(d.stream)
+        got = window(d)
+    finally:
+        d.close()
+    for a_, b_, k in zip(got, ref, ("w", "m", "v", "p")):
+        assert np.array_equal(a_, b_), k
+    for x, y in zip(states, ref_states):
+        assert np.array_equal(np.array(list(x.values()), np.float64).view(np.uint64),
+                              np.array(list(y.values()), np.float64).view(np.uint64))
