@@ -52,9 +52,11 @@ def parse():
                          "the median and the range as an extra key; 0 to skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0, help="chunk_elems of the plan (0: library default)")
-    ap.add_argument("--bind", choices=("flat", "tensors"), default="flat",
-                    help="bind the state as flat buffers, or through per-tensor pointer tables (same memory); "
-                         "with tensors the gradients are also bound per tensor, rebound before every micro-step")
+    ap.add_argument("--bind", choices=("flat", "tensors", "grads"), default="flat",
+                    help="bind every role as a flat buffer; every role through per-tensor pointer tables (same "
+                         "memory), the gradients rebound before every micro-step (tensors); or only the gradients "
+                         "per tensor, as a framework with per-tensor gradient buffers and the library's flat state "
+                         "would (grads)")
     ap.add_argument("--update", choices=("auto", "two-pass", "single-pass"), default="auto",
                     help="two-pass: reduce, statistics, then the update; single-pass: reduce, statistics and the "
                          "update in one read of the state (runs without clipping); auto: single-pass when the "
@@ -513,10 +515,10 @@ def run_gpu(w, steps: int, warmup: int, chunk: int = 0, calib: int = 0, bind: st
     off_bytes = [2 * int(x) for x in w.offsets[:-1]]
 
     def bind_grad(r, a):
-        # flat: one base per replica; tensors: one pointer per tensor, a new
+        # flat: one base per replica; tensors and grads: one pointer per tensor, a new
         # table before every micro-step as a framework with per-tensor
         # gradient buffers would bind them
-        if bind == "tensors":
+        if bind in ("tensors", "grads"):
             plan.bind_tensors("grad", [a + o for o in off_bytes], r)
         else:
             dp_plan_bind_flat(plan.handle, DP_ROLE_GRAD, r, a)
