@@ -35,8 +35,12 @@
  *    call inside the library is reported there, and hipGetLastError() is
  *    reset, so the caller's own HIP error checks do not see it again.  Faults inside
  *    kernels surface at the next synchronising call (dp_read_state).
- *  - One plan is used from one stream at a time; distinct plans are
- *    independent.
+ *  - Calls on one plan may be issued on different streams, one after
+ *    another: the caller orders them (for example with events), as the data
+ *    one call writes is read by the next.  The library orders only its own
+ *    pointer-table uploads across streams.  A HIP graph of captured calls is
+ *    ordered like any other launch on the stream it is launched on.
+ *    Distinct plans are independent.
  *  - A plan belongs to the device that is current at its first GPU call
  *    (binding per-tensor pointers, preparing a range, dp_state_init).  Every
  *    later GPU call checks that this device is current, and fails with
