@@ -866,7 +866,7 @@ def zero3_single_pass(steps: int, warmup: int, placements: int) -> dict:
     per_param = bytes_model(w, True)
     runs = []
     for k in range(placements):
-        elapsed, per_kind, state, _, _ = run_gpu(w, steps, warmup, single=True, spacer=k * (3 << 30))
+        elapsed, per_kind, _, _, _ = run_gpu(w, steps, warmup, single=True, spacer=k * (3 << 30))
         ms = elapsed * 1e3 / steps
         k_ms = per_kind["reduce_adamw"]["avg_ms"]
         k_gbps = launch_bytes(w, "reduce_adamw", True) / (k_ms * 1e-3) / 1e9

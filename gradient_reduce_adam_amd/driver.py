@@ -228,7 +228,7 @@ class DPStep:
         return "packed"
 
     def _spread_arrays(self, update, P: int, nacc: int) -> dict:
-        slot, offs, nbytes, acc_off, total = self._spread_plan(update, P, nacc)
+        _, offs, nbytes, acc_off, total = self._spread_plan(update, P, nacc)
         self.arena = torch.empty(total, dtype=torch.uint8, device=self.device)
         out = {}
         for (name, dt), off, nb in zip(update, offs, nbytes):
