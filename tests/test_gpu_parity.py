@@ -134,6 +134,19 @@ def test_tiny_workload_ten_steps():
     assert ref.scalars[-1]["t"] == 10
 
 
+def test_long_run_grows_the_scale_at_its_interval():
+    """2003 steps of the tiny workload's shape (65539 params) under a dynamic
+    loss scale with its full growth interval of 2000 clean steps: the scale
+    doubles once, at step 2000, and after every step the scalars, and at the
+    end master, m and v, equal the oracle's bit for bit."""
+    w = workloads.tiny().with_(numel=(65539,), scaler="dynamic", init_scale=1024.0, growth_interval=2000,
+                               steps=2003)
+    _, ref, states = _full_parity(w, w.steps)
+    scales = [s["scale"] for s in states]
+    assert scales[1998] == 1024.0 and scales[1999] == 2048.0 and scales[-1] == 2048.0
+    assert ref.scalars[-1]["t"] == 2003
+
+
 RAGGED = (3000, 17, 4096, 5, 70001, 256, 1, 65536, 131075)
 
 VARIANTS = {
